@@ -1,0 +1,136 @@
+"""Oracle GEMM: the plain definition of what the split-K decode GEMM computes.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): never imported by the
+product path.
+
+The split-K kernel on page
+``vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.gemm.splitk`` (module
+summary and ``SplitKGemm.kernel``) computes C = X . W^T with A = W (M, K) and
+B = X (N, K) both K-major ("kernel-M carries public N"). Each split rank sums
+one exact, contiguous K slice in FP32; the owner adds the peers' partials,
+casts once and stores once. That reaches, up to the order of rounding, the
+plain product
+
+    C[t, n] = sum_{k < K} X[t, k] * W[n, k]
+
+so the oracle is that product, evaluated in float64 on the bf16 operands
+(products of two bf16 values are exact in float64, and the float64 sum error
+is far below the acceptance bound). The result is *not* rounded to bf16: the
+acceptance bound covers the kernel's final RNE cast.
+
+The MXFP4 form decodes W first (``oracle.formats.mxfp4_dequant_f64``), as
+``fp4x8_bf16`` on page ``vllm.models.muse_spark.amd.mono.kernels.dev`` does
+before the bf16 MFMA.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .formats import bf16_bits_to_f64, mxfp4_dequant_f64
+
+
+def gemm_bf16_ref(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """C[T, N] float64 = X[T, K] . W[N, K]^T from bf16 bit patterns (uint16)."""
+    x = bf16_bits_to_f64(x_bits)
+    w = bf16_bits_to_f64(w_bits)
+    if x.ndim != 2 or w.ndim != 2 or x.shape[1] != w.shape[1]:
+        raise ValueError(f"shape mismatch X{x.shape} W{w.shape}")
+    return x @ w.T
+
+
+def gemm_rows_ref(x_bits: np.ndarray, w_bits_rows: np.ndarray) -> np.ndarray:
+    """Same product for a sample of weight rows: C[:, rows] of the full GEMM."""
+    return gemm_bf16_ref(x_bits, w_bits_rows)
+
+
+def gemm_mxfp4_ref(x_bits: np.ndarray, wq: np.ndarray, wscale: np.ndarray) -> np.ndarray:
+    """C[T, N] float64 = X . dequant(Wq, Wscale)^T."""
+    x = bf16_bits_to_f64(x_bits)
+    w = mxfp4_dequant_f64(wq, wscale)
+    if x.shape[1] != w.shape[1]:
+        raise ValueError(f"shape mismatch X{x.shape} W{w.shape}")
+    return x @ w.T
+
+
+def gemm_bruteforce(x_vals, w_vals) -> list:
+    """Pure-Python triple loop over float64 values, for tiny shapes only.
+
+    ``x_vals`` is a T x K and ``w_vals`` an N x K nested list (or array) of
+    numbers; returns the T x N nested list of dot products summed in K order.
+    """
+    t_n = len(x_vals)
+    n_n = len(w_vals)
+    out = []
+    for t in range(t_n):
+        row = []
+        for n in range(n_n):
+            acc = 0.0
+            for xv, wv in zip(x_vals[t], w_vals[n], strict=True):
+                acc += float(xv) * float(wv)
+            row.append(acc)
+        out.append(row)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Acceptance bound
+# ---------------------------------------------------------------------------
+
+
+def tolerance_bound(c_ref: np.ndarray, k: int, rms=None) -> np.ndarray:
+    """Per-element bound 2**-7 * |ref| + 1e-3 * sqrt(K) * rms(ref).
+
+    The bf16 RNE cast of the output contributes at most 2**-8 * |ref| (one
+    half unit in the last place of an 8-bit significand); the FP32
+    accumulation in an order the oracle does not fix contributes at most a
+    few units of 2**-24 per addend, summed over K addends and bounded in the
+    mean by sqrt(K) times the output scale. ``rms`` is the root mean square
+    of the whole reference output; pass it when ``c_ref`` is a sample.
+    """
+    c_ref = np.asarray(c_ref, dtype=np.float64)
+    if rms is None:
+        rms = math.sqrt(float(np.mean(c_ref * c_ref))) if c_ref.size else 0.0
+    return 2.0**-7 * np.abs(c_ref) + 1e-3 * math.sqrt(k) * rms
+
+
+def violation_ratio(c_test: np.ndarray, c_ref: np.ndarray, k: int, rms=None) -> float:
+    """max |test - ref| / bound (<= 1 passes). NaN anywhere counts as a failure."""
+    c_test = np.asarray(c_test, dtype=np.float64)
+    c_ref = np.asarray(c_ref, dtype=np.float64)
+    if c_test.shape != c_ref.shape:
+        raise ValueError(f"shape mismatch {c_test.shape} vs {c_ref.shape}")
+    if c_ref.size == 0:
+        return 0.0
+    if np.any(np.isnan(c_test)):
+        return math.inf
+    bound = tolerance_bound(c_ref, k, rms)
+    err = np.abs(c_test - c_ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(err == 0, 0.0, err / bound)
+    return float(np.max(r))
+
+
+# ---------------------------------------------------------------------------
+# Fixed-order wave reduction
+# ---------------------------------------------------------------------------
+
+
+def butterfly_f32(v: np.ndarray, offsets=(32, 16, 8, 4, 2, 1)) -> np.ndarray:
+    """Butterfly sum over the lanes of each 64-lane row of ``v`` in float32.
+
+    Step by step, in the order given, every lane i replaces its value with
+    value[i] + value[i ^ off], rounded to float32 (``butterfly`` / ``xred`` on
+    page ``vllm.models.deepseek_v41.amd.mono.common.ops``: the order of the
+    offsets is the numerical contract). ``v`` is float32 [rows, 64]; returns
+    the float32 [rows, 64] lane values after the last step.
+    """
+    v = np.array(v, dtype=np.float32, copy=True)
+    if v.ndim != 2 or v.shape[1] != 64:
+        raise ValueError("expected [rows, 64] lanes")
+    lanes = np.arange(64)
+    for off in offsets:
+        v = (v + v[:, lanes ^ off]).astype(np.float32)
+    return v

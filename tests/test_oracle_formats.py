@@ -1,0 +1,223 @@
+"""Pins for oracle/formats.py against things other than itself.
+
+Each conversion is checked against hand-worked fixtures under tests/golden/,
+an independent closed form, and (where one exists) a library routine, so that
+a plausible mistake (a wrong tie rule, nibble order, sign or bias) fails here.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+from tests.conftest import golden_rows
+
+# ---------------------------------------------------------------- bf16 -----
+
+
+def _torch_bf16_bits(x_f32):
+    t = torch.from_numpy(np.ascontiguousarray(x_f32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _structured_f32_patterns():
+    hi = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    lows = np.array([0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFE, 0xFFFF], dtype=np.uint32)
+    pats = (hi[:, None] | lows[None, :]).ravel()
+    rng = np.random.default_rng(7)
+    rnd = rng.integers(0, 1 << 32, size=1 << 21, dtype=np.uint64).astype(np.uint32)
+    return np.concatenate([pats, rnd])
+
+
+def test_bf16_golden_cases():
+    for f32_hex, bf16_hex, *_ in golden_rows("bf16_rne_cases.txt"):
+        x = np.array([int(f32_hex, 16)], dtype=np.uint32).view(np.float32)
+        got = int(F.f32_to_bf16_rne(x)[0])
+        assert got == int(bf16_hex, 16), (f32_hex, hex(got), bf16_hex)
+
+
+def test_bf16_matches_torch_and_integer_form():
+    pats = _structured_f32_patterns()
+    x = pats.view(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        got = F.f32_to_bf16_rne(x)
+    nan = np.isnan(x)
+    # library routine: torch's float32 -> bfloat16 cast rounds to nearest even
+    ref = _torch_bf16_bits(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # an independent closed form of RNE on the bit pattern (non-NaN inputs)
+    u = pats[~nan].astype(np.uint64)
+    closed = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    assert np.array_equal(got[~nan], closed)
+    # NaN stays NaN
+    assert np.all(np.isnan(F.bf16_bits_to_f64(got[nan])))
+
+
+def test_bf16_widening_exhaustive():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = F.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert np.all(same)
+    assert np.array_equal(np.signbit(got[~np.isnan(got)]), np.signbit(ref[~np.isnan(ref)]))
+
+
+def test_bf16_pair_word_layout():
+    # bf16(a) in the low half, bf16(b) in the high half (bf16_pair)
+    w = F.bf16_pair_word(np.float32([1.0]), np.float32([-2.0]))
+    assert int(w[0]) == 0xC0003F80
+
+
+# ---------------------------------------------------------------- E4M3 -----
+
+
+def test_e4m3_golden_cases():
+    for val, code, *_ in golden_rows("e4m3_cases.txt"):
+        got = int(F.f32_to_e4m3_rne(np.float32([float(val)]))[0])
+        assert got == int(code, 16), (val, hex(got), code)
+
+
+def test_e4m3_pack4_golden():
+    for a, b, c, d, word in golden_rows("e4m3_pack4_cases.txt"):
+        got = int(F.e4m3_pack4_word(*[np.float32([float(v)]) for v in (a, b, c, d)])[0])
+        assert got == int(word, 16), (a, b, c, d, hex(got), word)
+
+
+def test_e4m3_values_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    got = F.e4m3_value(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert np.all(same)
+    assert F.e4m3_value(np.array([0x7E]))[0] == 448.0
+
+
+def _e4m3_probe_values():
+    mags = F.e4m3_value(np.arange(0x7F))  # all finite non-negative values
+    mids = (mags[:-1] + mags[1:]) / 2
+    vals = np.concatenate([mags, mids]).astype(np.float32)
+    up = np.nextafter(vals, np.float32(np.inf))
+    dn = np.nextafter(vals, np.float32(0))
+    rng = np.random.default_rng(3)
+    rnd = (rng.random(1 << 16) * 448).astype(np.float32)
+    v = np.concatenate([vals, up, dn, rnd])
+    v = v[np.abs(v) <= 448]
+    return np.concatenate([v, -v])
+
+
+def test_e4m3_rne_matches_torch():
+    v = _e4m3_probe_values()
+    got = F.f32_to_e4m3_rne(v)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_rejects_out_of_range():
+    with pytest.raises(ValueError):
+        F.f32_to_e4m3_rne(np.float32([449.0]))
+
+
+# ------------------------------------------------------- E2M1 / E8M0 -------
+
+
+def test_e2m1_all_codes():
+    vals = F.e2m1_value(np.arange(16))
+    assert list(vals[:8]) == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(vals[8:]) == [-v for v in vals[:8]]
+    assert math.copysign(1.0, vals[8]) == -1.0  # code 8 is -0
+    assert np.all(np.diff(vals[:8]) > 0)
+    # torch's E2M1 pair type as a library cross-check (unpack by its own rule)
+    if hasattr(torch, "float4_e2m1fn_x2"):
+        try:
+            t = torch.arange(16, dtype=torch.uint8).view(torch.float4_e2m1fn_x2)
+            ref = t.to(torch.float32)  # not every build implements this cast
+        except (RuntimeError, TypeError, NotImplementedError):
+            ref = None
+        if ref is not None and ref.numel() == 16:
+            assert np.array_equal(ref.numpy().astype(np.float64), vals)
+
+
+def test_e8m0_closed_form_and_library():
+    codes = np.arange(255)
+    got = F.e8m0_value(codes)
+    for c in range(255):
+        assert got[c] == math.ldexp(1.0, c - 127)
+    # the helper's bit form: code << 23 read as float32, for codes 1..254
+    bits = (np.arange(1, 255, dtype=np.uint32) << np.uint32(23)).view(np.float32)
+    assert np.array_equal(got[1:255], bits.astype(np.float64))
+    assert np.isnan(F.e8m0_value(np.array([255]))[0])
+    if hasattr(torch, "float8_e8m0fnu"):
+        ref = torch.arange(1, 256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e8m0fnu)
+        ref = ref.double().numpy()
+        g = F.e8m0_value(np.arange(1, 256))
+        assert np.all((g == ref) | (np.isnan(g) & np.isnan(ref)))
+
+
+# ------------------------------------------------------------- MXFP4 -------
+
+
+def _dword_rows(word_hex):
+    w = np.array([int(word_hex, 16)], dtype=np.uint32)
+    return w.view(np.uint8).reshape(1, 4)  # little-endian bytes of one dword
+
+
+def test_mxfp4_golden_cases():
+    for row in golden_rows("mxfp4_cases.txt"):
+        word, code, vals = row[0], int(row[1]), [float(v) for v in row[2:]]
+        wq = np.tile(_dword_rows(word), (1, 4))  # 32 elements: the dword 4 times
+        ws = np.array([[code]], dtype=np.uint8)
+        got = F.mxfp4_dequant_f64(wq, ws)[0, :8]
+        assert list(got) == vals, (word, code, list(got))
+        assert list(np.signbit(got)) == [math.copysign(1.0, v) < 0 for v in vals]
+
+
+def test_mxfp4_bruteforce_small():
+    rng = np.random.default_rng(11)
+    n, k = 3, 64
+    wq = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    ws = rng.integers(110, 140, size=(n, k // 32), dtype=np.uint8)
+    table = {0: 0.0, 1: 0.5, 2: 1.0, 3: 1.5, 4: 2.0, 5: 3.0, 6: 4.0, 7: 6.0}
+    got = F.mxfp4_dequant_f64(wq, ws)
+    for r in range(n):
+        for c in range(k):
+            byte = int(wq[r][c // 2])
+            nib = (byte & 15) if c % 2 == 0 else (byte >> 4)
+            mag = table[nib & 7]
+            val = (-mag if nib & 8 else mag) * 2.0 ** (int(ws[r][c // 32]) - 127)
+            assert got[r][c] == val
+
+
+def test_mxfp4_bf16_exact_range():
+    # every (code, scale) pair with scale in [2, 252] decodes exactly to bf16
+    codes = np.arange(16, dtype=np.uint8)
+    scales = np.arange(2, 253, dtype=np.uint8)
+    n = len(scales)
+    nib = np.tile(codes, 2)  # 32 elements per row: each code twice
+    wq = (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
+    wq = np.tile(wq, (n, 1))
+    ws = scales.reshape(n, 1)
+    bits = F.mxfp4_dequant_bf16_bits(wq, ws)
+    vals = F.bf16_bits_to_f64(bits)
+    expect = F.e2m1_value(nib)[None, :] * np.ldexp(1.0, (scales.astype(int) - 127))[:, None]
+    assert np.array_equal(vals, expect)
+
+
+# ------------------------------------------------ planted mistakes ---------
+
+
+def test_pins_catch_planted_mistakes():
+    """Wrong variants of the oracle, planted here on the CPU, must fail the pins."""
+    # truncation instead of RNE fails the bf16 fixtures
+    x = np.array([0x3F818000], dtype=np.uint32).view(np.float32)
+    trunc = (x.view(np.uint32) >> 16).astype(np.uint16)
+    assert int(trunc[0]) != 0x3F82 and int(F.f32_to_bf16_rne(x)[0]) == 0x3F82
+    # high-nibble-first decode fails the MXFP4 fixture
+    wq = np.tile(_dword_rows("0x76543210"), (1, 4))
+    swapped = np.empty((1, 32), dtype=np.uint8)
+    swapped[:, 0::2] = wq >> 4
+    swapped[:, 1::2] = wq & 15
+    assert list(F.e2m1_value(swapped[0, :8])) != [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    # a scale bias of 128 instead of 127 fails the E8M0 closed form
+    assert F.e8m0_value(np.array([127]))[0] == 1.0 != 2.0 ** (127 - 128)
