@@ -1,0 +1,168 @@
+/*
+ * skgemm -- split-K decode GEMM for AMD MI355X (gfx950, CDNA4).
+ *
+ * C ABI of libskgemm.so. Plain pointers and sizes only; every pointer passed
+ * to a compute entry point is DEVICE memory owned by the caller (for example
+ * the storage of a torch tensor). The library never frees, reallocates or
+ * synchronises caller memory. Work is enqueued on the caller's stream and
+ * nothing is synchronised on return, as with the graph-compatible launch
+ * wrapper on page vllm.models.common.ops.moe_tail_fusion.primitives
+ * (CUDAGraphCompatibleWrapper: launch on the current stream, no producer
+ * sync).
+ *
+ * The operation (page
+ * vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.gemm.splitk, module
+ * summary and SplitKGemm): C[T, N] = X[T, K] . W[N, K]^T. Each of split_k
+ * contiguous, equal K slices is accumulated in FP32; the slices' partials are
+ * reduced once in slice order, rounded to bf16 (round to nearest even) and C
+ * is stored once. The weights take the MFMA's row operand ("kernel-M carries
+ * public N").
+ *
+ * Layouts (row-major, the last index contiguous):
+ *   W      bf16  [N, K]     (K contiguous; SplitKGemm.kernel: A is K-major)
+ *   X      bf16  [T, K]     (K contiguous; B is K-major)
+ *   C      bf16  [T, N]     (N contiguous)
+ *   Wq     uint8 [N, K/2]   two E2M1 codes per byte: element k of a row is in
+ *                           byte k/2, the low nibble when k is even (page
+ *                           vllm.models.muse_spark.amd.mono.kernels.dev,
+ *                           fp4x8_bf16: a dword of 8 E2M1, low nibble first)
+ *   Wscale uint8 [N, K/32]  one E8M0 code per 32-element K block; code c
+ *                           stands for 2^(c-127) (same page, e8m0_f32).
+ *                           Codes must lie in 1..254.
+ *
+ * Return codes: 0 on success, a negative SKGEMM_E* code otherwise. When an
+ * argument check fails nothing is enqueued and C is untouched. Faults of the
+ * enqueued work surface asynchronously on the caller's stream.
+ *
+ * Concurrency: calls on one stream are ordered by the stream. Each
+ * (device, stream) pair owns its own split-K workspace, so calls on different
+ * streams do not share partial buffers.
+ */
+#ifndef SKGEMM_H
+#define SKGEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t; /* HIP's own stream handle type */
+
+#define SKGEMM_API __attribute__((visibility("default")))
+
+enum skgemm_status {
+  SKGEMM_OK = 0,
+  SKGEMM_EINVAL = -1, /* null pointer, negative size, split_k not in {1,2,4,8} */
+  SKGEMM_EALIGN = -2, /* a pointer is not 16-byte aligned                      */
+  SKGEMM_ESHAPE = -3, /* N % 16, K % (32*split_k) (bf16) or K % (128*split_k)
+                         (MXFP4) non-zero, or a size above the limits below   */
+  SKGEMM_ENOMEM = -4, /* split-K workspace could not be allocated, or it would
+                         have to grow while the stream is being captured      */
+  SKGEMM_EHIP = -5    /* a HIP runtime call failed; see skgemm_last_hip_error */
+};
+
+/* Size limits (checked; SKGEMM_ESHAPE beyond them). T has no upper limit:
+ * token counts above 128 are processed in blocks of 128 rows. */
+#define SKGEMM_MAX_N (1 << 18)
+#define SKGEMM_MAX_K (1 << 22)
+
+/*
+ * skgemm_bf16: C = X . W^T with bf16 W, X, C and FP32 accumulation.
+ *   W, X, C  device pointers, 16-byte aligned, layouts above.
+ *   T >= 0   tokens (rows of X and C). T == 0 or N == 0 enqueues nothing.
+ *   N >= 0   output features, N % 16 == 0.
+ *   K >= 0   reduction length, K % (32 * split_k) == 0. K == 0 stores zeros.
+ *   split_k  1, 2, 4 or 8: number of contiguous K slices, slice r covering
+ *            [r*K/split_k, (r+1)*K/split_k) (SplitKGemm.kernel splits K evenly
+ *            over the cluster ranks; shapes are validated, never padded).
+ *   stream   HIP stream to enqueue on (0 = the null stream).
+ * With split_k > 1 the first call on a stream allocates that stream's
+ * workspace (see skgemm_reserve) unless one large enough exists.
+ */
+SKGEMM_API int skgemm_bf16(const void* W, const void* X, void* C, int T, int N, int K,
+                           int split_k, hipStream_t stream);
+
+/*
+ * skgemm_mxfp4: C = X . dequant(Wq, Wscale)^T. The weights are decoded exactly
+ * to bf16 in registers (E2M1 value times 2^(code-127)), then multiplied as in
+ * skgemm_bf16 (page vllm.models.muse_spark.amd.mono.kernels.dev, fp4x8_bf16).
+ *   Wq, X, C 16-byte aligned; Wscale needs no alignment.
+ *   K % (128 * split_k) == 0 (each lane decodes 32 consecutive K elements,
+ *   one whole scale block, per 16-byte load). Other arguments as skgemm_bf16.
+ */
+SKGEMM_API int skgemm_mxfp4(const void* Wq, const void* Wscale, const void* X, void* C, int T,
+                            int N, int K, int split_k, hipStream_t stream);
+
+/*
+ * skgemm_reserve: make sure the workspace of (current device, stream) can
+ * serve any call with T <= max_T (capped at 128, the block size), N <= max_N
+ * and split_k <= max_split_k. Call it before capturing a stream into a HIP
+ * graph: inside a capture the workspace can not grow (SKGEMM_ENOMEM). The
+ * workspace is FP32 partials [split_k, min(T,128), N] and one uint32 counter
+ * per output tile; counters return to zero at the end of every call.
+ * May synchronise `stream` when it replaces a smaller workspace.
+ */
+SKGEMM_API int skgemm_reserve(int max_T, int max_N, int max_split_k, hipStream_t stream);
+
+/* skgemm_release: free every workspace of the calling process. Synchronises
+ * the device first. Not to be called while other threads enqueue work. */
+SKGEMM_API int skgemm_release(void);
+
+/*
+ * skgemm_mxfp4_dequant: W_out bf16 [N, K] = E2M1(Wq) * 2^(Wscale - 127),
+ * elementwise, exact (the decode the GEMM applies in registers; exported for
+ * bit-exact testing). K % 32 == 0, Wq and W_out 16-byte aligned.
+ */
+SKGEMM_API int skgemm_mxfp4_dequant(const void* Wq, const void* Wscale, void* W_out, int N, int K,
+                                    hipStream_t stream);
+
+/*
+ * skgemm_pack_bf16: out[i] = bf16(in[2i]) | bf16(in[2i+1]) << 16, round to
+ * nearest even, the epilogue's packing (page
+ * vllm.models.muse_spark.amd.mono.kernels.dev, bf16_pair). in: float
+ * [2*n_pairs], out: uint32 [n_pairs], device memory, 16-byte aligned.
+ */
+SKGEMM_API int skgemm_pack_bf16(const float* in, uint32_t* out, size_t n_pairs, hipStream_t stream);
+
+/*
+ * skgemm_pack_e4m3: out[i] = four OCP E4M3FN bytes of in[4i..4i+3], the first
+ * in the low byte, round to nearest even; inputs must satisfy |x| <= 448
+ * (page vllm.models.deepseek_v41.amd.mono.common.ops, fp8_pack4: "already in
+ * range"). in: float [4*n_quads], out: uint32 [n_quads], 16-byte aligned.
+ */
+SKGEMM_API int skgemm_pack_e4m3(const float* in, uint32_t* out, size_t n_quads, hipStream_t stream);
+
+/*
+ * skgemm_wave_sum: for each group of 64 floats, every lane of one wavefront
+ * ends with the butterfly sum over lane offsets 32, 16, 8, 4, 2, 1 in that
+ * order, each step value[i] + value[i ^ off] in FP32 (page
+ * vllm.models.deepseek_v41.amd.mono.common.ops, butterfly / xred / xshfl:
+ * the order is the numerical contract; 32 and 16 go through
+ * v_permlane32/16_swap, the rest through DPP). in, out: float [64*n_waves].
+ */
+SKGEMM_API int skgemm_wave_sum(const float* in, float* out, size_t n_waves, hipStream_t stream);
+
+/*
+ * skgemm_tactic_for: describe, as a short JSON object written to buf
+ * (NUL-terminated, truncated to buf_len), the kernel configuration a call with
+ * these sizes would launch. mxfp4 != 0 selects the MXFP4 entry point. Returns
+ * the same code the compute call's argument checks would (pointers excluded).
+ * Host only; touches no device.
+ */
+SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int mxfp4, char* buf,
+                                 size_t buf_len);
+
+/* skgemm_strerror: static text for a return code. */
+SKGEMM_API const char* skgemm_strerror(int code);
+
+/* skgemm_last_hip_error: the hipError_t of the last SKGEMM_EHIP on this
+ * thread (0 if none). */
+SKGEMM_API int skgemm_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKGEMM_H */

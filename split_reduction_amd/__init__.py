@@ -1,0 +1,156 @@
+"""Python binding of libskgemm.so, the split-K decode GEMM for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/skgemm.h``. Functions carry the
+C names and argument order; array arguments may be torch tensors on the GPU
+(their storage address is passed) or plain integer device addresses. The
+stream defaults to torch's current stream on the current device.
+
+The library is loaded on first use. If it is missing or fails to load, every
+call raises ``SkgemmError``: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libskgemm.so")
+
+SKGEMM_OK = 0
+SKGEMM_EINVAL = -1
+SKGEMM_EALIGN = -2
+SKGEMM_ESHAPE = -3
+SKGEMM_ENOMEM = -4
+SKGEMM_EHIP = -5
+
+_lib = None
+
+
+class SkgemmError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(what)
+
+
+def _declare(lib):
+    vp, i, sz, st = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    sig = {
+        "skgemm_bf16": [vp, vp, vp, i, i, i, i, st],
+        "skgemm_mxfp4": [vp, vp, vp, vp, i, i, i, i, st],
+        "skgemm_reserve": [i, i, i, st],
+        "skgemm_release": [],
+        "skgemm_mxfp4_dequant": [vp, vp, vp, i, i, st],
+        "skgemm_pack_bf16": [vp, vp, sz, st],
+        "skgemm_pack_e4m3": [vp, vp, sz, st],
+        "skgemm_wave_sum": [vp, vp, sz, st],
+        "skgemm_tactic_for": [i, i, i, i, i, ctypes.c_char_p, sz],
+        "skgemm_last_hip_error": [],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.skgemm_strerror.argtypes = [ctypes.c_int]
+    lib.skgemm_strerror.restype = ctypes.c_char_p
+
+
+def lib():
+    """The loaded libskgemm.so (raises SkgemmError if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise SkgemmError(SKGEMM_EHIP, f"{LIB_PATH} is not built (run split_reduction_amd/build.py)")
+        try:
+            handle = ctypes.CDLL(LIB_PATH)
+        except OSError as e:
+            raise SkgemmError(SKGEMM_EHIP, f"cannot load {LIB_PATH}: {e}") from e
+        _declare(handle)
+        _lib = handle
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().skgemm_strerror(code).decode()
+
+
+def _check(code: int, name: str) -> None:
+    if code != SKGEMM_OK:
+        extra = ""
+        if code == SKGEMM_EHIP:
+            extra = f" (hipError {lib().skgemm_last_hip_error()})"
+        raise SkgemmError(code, f"{name}: {strerror(code)}{extra}")
+
+
+def _ptr(a) -> int:
+    if a is None:
+        return 0
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def skgemm_bf16(W, X, C, T: int, N: int, K: int, split_k: int, stream=None) -> None:
+    """C[T, N] = X[T, K] . W[N, K]^T (bf16 in and out, FP32 accumulation)."""
+    code = lib().skgemm_bf16(_ptr(W), _ptr(X), _ptr(C), T, N, K, split_k, _stream(stream))
+    _check(code, "skgemm_bf16")
+
+
+def skgemm_mxfp4(Wq, Wscale, X, C, T: int, N: int, K: int, split_k: int, stream=None) -> None:
+    """C = X . dequant(Wq, Wscale)^T with MXFP4 weights decoded in registers."""
+    code = lib().skgemm_mxfp4(_ptr(Wq), _ptr(Wscale), _ptr(X), _ptr(C), T, N, K, split_k,
+                              _stream(stream))
+    _check(code, "skgemm_mxfp4")
+
+
+def skgemm_reserve(max_T: int, max_N: int, max_split_k: int, stream=None) -> None:
+    _check(lib().skgemm_reserve(max_T, max_N, max_split_k, _stream(stream)), "skgemm_reserve")
+
+
+def skgemm_release() -> None:
+    _check(lib().skgemm_release(), "skgemm_release")
+
+
+def skgemm_mxfp4_dequant(Wq, Wscale, W_out, N: int, K: int, stream=None) -> None:
+    code = lib().skgemm_mxfp4_dequant(_ptr(Wq), _ptr(Wscale), _ptr(W_out), N, K, _stream(stream))
+    _check(code, "skgemm_mxfp4_dequant")
+
+
+def skgemm_pack_bf16(inp, out, n_pairs: int, stream=None) -> None:
+    _check(lib().skgemm_pack_bf16(_ptr(inp), _ptr(out), n_pairs, _stream(stream)), "skgemm_pack_bf16")
+
+
+def skgemm_pack_e4m3(inp, out, n_quads: int, stream=None) -> None:
+    _check(lib().skgemm_pack_e4m3(_ptr(inp), _ptr(out), n_quads, _stream(stream)), "skgemm_pack_e4m3")
+
+
+def skgemm_wave_sum(inp, out, n_waves: int, stream=None) -> None:
+    _check(lib().skgemm_wave_sum(_ptr(inp), _ptr(out), n_waves, _stream(stream)), "skgemm_wave_sum")
+
+
+def skgemm_tactic_for(T: int, N: int, K: int, split_k: int, mxfp4: bool = False) -> dict:
+    """The launch configuration a call with these sizes uses (host only)."""
+    buf = ctypes.create_string_buffer(512)
+    code = lib().skgemm_tactic_for(T, N, K, split_k, 1 if mxfp4 else 0, buf, len(buf))
+    _check(code, "skgemm_tactic_for")
+    return json.loads(buf.value.decode())
+
+
+def skgemm_strerror(code: int) -> str:
+    return strerror(code)
+
+
+def skgemm_last_hip_error() -> int:
+    return lib().skgemm_last_hip_error()

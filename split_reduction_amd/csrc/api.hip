@@ -1,0 +1,246 @@
+// C ABI of libskgemm.so: argument checks, split-K workspace ownership, token
+// blocking and kernel dispatch. Declarations and contracts: include/skgemm.h.
+
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/skgemm.h"
+#include "skgemm_internal.h"
+
+namespace {
+
+constexpr int kTokenBlock = 128;  // rows of X / C per launch (16 * 8 MFMA tiles)
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return SKGEMM_EHIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Argument checks shared by both GEMM entry points and the tactic query.
+// Pointers are checked only when check_ptrs is set.
+int check_gemm(bool mx, const void* w, const void* ws, const void* x, const void* c, int T, int N,
+               int K, int S, bool check_ptrs) {
+  if (T < 0 || N < 0 || K < 0) return SKGEMM_EINVAL;
+  if (S != 1 && S != 2 && S != 4 && S != 8) return SKGEMM_EINVAL;
+  if (N % 16 != 0) return SKGEMM_ESHAPE;
+  if (K % ((mx ? 128 : 32) * S) != 0) return SKGEMM_ESHAPE;
+  if (N > SKGEMM_MAX_N || K > SKGEMM_MAX_K) return SKGEMM_ESHAPE;
+  if (!check_ptrs || T == 0 || N == 0) return SKGEMM_OK;
+  if (c == nullptr) return SKGEMM_EINVAL;
+  if (!aligned16(c)) return SKGEMM_EALIGN;
+  if (K > 0) {
+    if (w == nullptr || x == nullptr || (mx && ws == nullptr)) return SKGEMM_EINVAL;
+    if (!aligned16(w) || !aligned16(x)) return SKGEMM_EALIGN;
+  }
+  return SKGEMM_OK;
+}
+
+// ---- split-K workspace: one per (device, stream) ---------------------------
+
+struct Workspace {
+  float* part = nullptr;
+  size_t part_bytes = 0;
+  uint32_t* cnt = nullptr;
+  size_t cnt_count = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+// Makes the stream's workspace hold at least part_bytes of partials and
+// cnt_count zeroed counters. Growing frees the old buffers after the stream
+// drains; under graph capture it refuses instead.
+int ensure_workspace(hipStream_t stream, size_t part_bytes, size_t cnt_count, Workspace* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& w = g_ws[std::make_pair(dev, stream)];
+  if (w.part_bytes >= part_bytes && w.cnt_count >= cnt_count) {
+    *out = w;
+    return SKGEMM_OK;
+  }
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &st);
+  if (e != hipSuccess) return hip_fail(e);
+  if (st != hipStreamCaptureStatusNone) return SKGEMM_ENOMEM;
+  if (w.part != nullptr || w.cnt != nullptr) {
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (w.part) (void)hipFree(w.part);
+    if (w.cnt) (void)hipFree(w.cnt);
+    w = Workspace{};
+  }
+  Workspace nw;
+  nw.part_bytes = std::max(part_bytes, (size_t)256);
+  nw.cnt_count = std::max(cnt_count, (size_t)64);
+  if (hipMalloc((void**)&nw.part, nw.part_bytes) != hipSuccess) return SKGEMM_ENOMEM;
+  if (hipMalloc((void**)&nw.cnt, nw.cnt_count * sizeof(uint32_t)) != hipSuccess) {
+    (void)hipFree(nw.part);
+    return SKGEMM_ENOMEM;
+  }
+  e = hipMemsetAsync(nw.cnt, 0, nw.cnt_count * sizeof(uint32_t), stream);
+  if (e != hipSuccess) {
+    (void)hipFree(nw.part);
+    (void)hipFree(nw.cnt);
+    return hip_fail(e);
+  }
+  w = nw;
+  *out = w;
+  return SKGEMM_OK;
+}
+
+size_t part_bytes_for(int T, int N, int S) {
+  return (size_t)S * (size_t)std::min(T, kTokenBlock) * (size_t)N * sizeof(float);
+}
+size_t counters_for(int N) { return (size_t)N / 16; }
+
+int run_gemm(bool mx, const void* w, const void* ws, const void* x, void* c, int T, int N, int K,
+             int S, hipStream_t stream) {
+  int rc = check_gemm(mx, w, ws, x, c, T, N, K, S, true);
+  if (rc != SKGEMM_OK) return rc;
+  if (T == 0 || N == 0) return SKGEMM_OK;
+  Workspace wsp;
+  if (S > 1) {
+    rc = ensure_workspace(stream, part_bytes_for(T, N, S), counters_for(N), &wsp);
+    if (rc != SKGEMM_OK) return rc;
+  }
+  for (int t0 = 0; t0 < T; t0 += kTokenBlock) {
+    const int tb = std::min(kTokenBlock, T - t0);
+    skg::Tactic tac;
+    if (!skg::pick_tactic(tb, N, K, S, mx, &tac)) return SKGEMM_ESHAPE;
+    skg::GemmParams p{};
+    p.w = w;
+    p.wscale = static_cast<const uint8_t*>(ws);
+    p.x = static_cast<const uint8_t*>(x) + (size_t)t0 * (size_t)K * 2;
+    p.c = static_cast<uint8_t*>(c) + (size_t)t0 * (size_t)N * 2;
+    p.part = wsp.part;
+    p.cnt = wsp.cnt;
+    p.T = tb;
+    p.N = N;
+    p.K = K;
+    p.S = S;
+    p.ks = K / S;
+    p.kc = tac.kc;
+    p.nchunks = (tac.kc > 0) ? p.ks / tac.kc : 0;
+    hipError_t e = skg::launch_gemm(tac, p, stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return SKGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+SKGEMM_API int skgemm_bf16(const void* W, const void* X, void* C, int T, int N, int K,
+                           int split_k, hipStream_t stream) {
+  return run_gemm(false, W, nullptr, X, C, T, N, K, split_k, stream);
+}
+
+SKGEMM_API int skgemm_mxfp4(const void* Wq, const void* Wscale, const void* X, void* C, int T,
+                            int N, int K, int split_k, hipStream_t stream) {
+  return run_gemm(true, Wq, Wscale, X, C, T, N, K, split_k, stream);
+}
+
+SKGEMM_API int skgemm_reserve(int max_T, int max_N, int max_split_k, hipStream_t stream) {
+  if (max_T < 0 || max_N < 0 || max_split_k < 1 || max_split_k > 8) return SKGEMM_EINVAL;
+  if (max_N > SKGEMM_MAX_N) return SKGEMM_ESHAPE;
+  Workspace w;
+  return ensure_workspace(stream, part_bytes_for(max_T, max_N, max_split_k), counters_for(max_N),
+                          &w);
+}
+
+SKGEMM_API int skgemm_release(void) {
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  int rc = SKGEMM_OK;
+  for (auto& kv : g_ws) {
+    hipError_t e = hipSetDevice(kv.first.first);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) rc = hip_fail(e);
+    if (kv.second.part) (void)hipFree(kv.second.part);
+    if (kv.second.cnt) (void)hipFree(kv.second.cnt);
+  }
+  g_ws.clear();
+  return rc;
+}
+
+SKGEMM_API int skgemm_mxfp4_dequant(const void* Wq, const void* Wscale, void* W_out, int N, int K,
+                                    hipStream_t stream) {
+  if (N < 0 || K < 0) return SKGEMM_EINVAL;
+  if (K % 32 != 0) return SKGEMM_ESHAPE;
+  if (N == 0 || K == 0) return SKGEMM_OK;
+  if (!Wq || !Wscale || !W_out) return SKGEMM_EINVAL;
+  if (!aligned16(Wq) || !aligned16(W_out)) return SKGEMM_EALIGN;
+  hipError_t e = skg::launch_mxfp4_dequant(Wq, Wscale, W_out, N, K, stream);
+  return e == hipSuccess ? SKGEMM_OK : hip_fail(e);
+}
+
+SKGEMM_API int skgemm_pack_bf16(const float* in, uint32_t* out, size_t n_pairs, hipStream_t stream) {
+  if (n_pairs == 0) return SKGEMM_OK;
+  if (!in || !out) return SKGEMM_EINVAL;
+  if (!aligned16(in) || !aligned16(out)) return SKGEMM_EALIGN;
+  hipError_t e = skg::launch_pack_bf16(in, out, n_pairs, stream);
+  return e == hipSuccess ? SKGEMM_OK : hip_fail(e);
+}
+
+SKGEMM_API int skgemm_pack_e4m3(const float* in, uint32_t* out, size_t n_quads, hipStream_t stream) {
+  if (n_quads == 0) return SKGEMM_OK;
+  if (!in || !out) return SKGEMM_EINVAL;
+  if (!aligned16(in) || !aligned16(out)) return SKGEMM_EALIGN;
+  hipError_t e = skg::launch_pack_e4m3(in, out, n_quads, stream);
+  return e == hipSuccess ? SKGEMM_OK : hip_fail(e);
+}
+
+SKGEMM_API int skgemm_wave_sum(const float* in, float* out, size_t n_waves, hipStream_t stream) {
+  if (n_waves == 0) return SKGEMM_OK;
+  if (!in || !out) return SKGEMM_EINVAL;
+  if (!aligned16(in) || !aligned16(out)) return SKGEMM_EALIGN;
+  hipError_t e = skg::launch_wave_sum(in, out, n_waves, stream);
+  return e == hipSuccess ? SKGEMM_OK : hip_fail(e);
+}
+
+SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int mxfp4, char* buf,
+                                 size_t buf_len) {
+  const bool mx = mxfp4 != 0;
+  int rc = check_gemm(mx, nullptr, nullptr, nullptr, nullptr, T, N, K, split_k, false);
+  if (rc != SKGEMM_OK) return rc;
+  skg::Tactic t{};
+  const int tb = std::min(std::max(T, 1), kTokenBlock);
+  if (!skg::pick_tactic(tb, N, K, split_k, mx, &t)) return SKGEMM_ESHAPE;
+  const int blocks = (T + kTokenBlock - 1) / kTokenBlock;
+  if (buf != nullptr && buf_len > 0) {
+    snprintf(buf, buf_len,
+             "{\"nt\": %d, \"rg\": %d, \"wk\": %d, \"wn\": %d, \"d\": %d, \"kc\": %d, "
+             "\"tile_n\": %d, \"threads\": %d, \"lds\": %d, \"grid\": %d, \"split_k\": %d, "
+             "\"token_blocks\": %d, \"mxfp4\": %d}",
+             t.nt, t.rg, t.wk, t.wn, t.d, t.kc, t.tile_n, t.threads, t.lds, t.grid, split_k,
+             blocks, t.mx);
+  }
+  return SKGEMM_OK;
+}
+
+SKGEMM_API const char* skgemm_strerror(int code) {
+  switch (code) {
+    case SKGEMM_OK: return "success";
+    case SKGEMM_EINVAL: return "invalid argument (null pointer, negative size or split_k not in {1,2,4,8})";
+    case SKGEMM_EALIGN: return "pointer not 16-byte aligned";
+    case SKGEMM_ESHAPE: return "unsupported shape (N % 16, K % (32*split_k) or K % (128*split_k) for MXFP4, or size limit)";
+    case SKGEMM_ENOMEM: return "split-K workspace could not be allocated (or must grow during stream capture: call skgemm_reserve first)";
+    case SKGEMM_EHIP: return "HIP runtime error (see skgemm_last_hip_error)";
+  }
+  return "unknown skgemm status";
+}
+
+SKGEMM_API int skgemm_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Kernels that expose the device helpers on their own, for bit-exact checks:
+// bf16 and E4M3 packing, the fixed-order wave sum and the MXFP4 decode. They
+// run the same inline helpers the GEMM kernels use.
+
+#include "device/mxfp4.h"
+#include "device/pack.h"
+#include "device/types.h"
+#include "device/wave.h"
+#include "skgemm_internal.h"
+
+namespace skg {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void pack_bf16_kernel(const float* in, uint32_t* out,
+                                                             size_t n) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const float2 v = reinterpret_cast<const float2*>(in)[i];
+  out[i] = bf16_pair(v.x, v.y);
+}
+
+__global__ __launch_bounds__(kThreads) void pack_e4m3_kernel(const float* in, uint32_t* out,
+                                                             size_t n) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const float4 v = reinterpret_cast<const float4*>(in)[i];
+  out[i] = e4m3_pack4(v.x, v.y, v.z, v.w);
+}
+
+// One wavefront per group of 64 values; every lane runs the butterfly (the
+// grid covers whole wavefronts, so no lane of a wave is inactive).
+__global__ __launch_bounds__(kThreads) void wave_sum_kernel(const float* in, float* out,
+                                                            size_t n_waves) {
+  const size_t wave = (size_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;
+  const int lane = threadIdx.x & 63;
+  if (wave >= n_waves) return;  // uniform across the wave
+  const float v = in[wave * 64 + lane];
+  out[wave * 64 + lane] = butterfly_sum(v);
+}
+
+// One thread per dword of 8 codes: W_out[n, 8i .. 8i+7] = decode(Wq dword i
+// of row n, scale of its 32-element block).
+__global__ __launch_bounds__(kThreads) void mxfp4_dequant_kernel(const uint32_t* wq,
+                                                                 const uint8_t* ws, u32x4* out,
+                                                                 int N, int K) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t dwords_per_row = (size_t)K / 8;
+  if (i >= (size_t)N * dwords_per_row) return;
+  const size_t row = i / dwords_per_row;
+  const size_t col = i % dwords_per_row;  // elements 8 col .. 8 col + 7
+  const uint32_t code = ws[row * (K / 32) + col / 4];
+  const bf16x8 v = fp4x8_bf16(wq[i], e8m0_f32(code));
+  out[i] = __builtin_bit_cast(u32x4, v);
+}
+
+unsigned blocks_for(size_t n, size_t per_block) {
+  return (unsigned)((n + per_block - 1) / per_block);
+}
+
+}  // namespace
+
+hipError_t launch_pack_bf16(const float* in, uint32_t* out, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks_for(n, kThreads)), dim3(kThreads), 0, s, in,
+                     out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_e4m3(const float* in, uint32_t* out, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_e4m3_kernel, dim3(blocks_for(n, kThreads)), dim3(kThreads), 0, s, in,
+                     out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_wave_sum(const float* in, float* out, size_t n_waves, hipStream_t s) {
+  if (n_waves == 0) return hipSuccess;
+  hipLaunchKernelGGL(wave_sum_kernel, dim3(blocks_for(n_waves, kThreads / 64)), dim3(kThreads), 0,
+                     s, in, out, n_waves);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_dequant(const void* wq, const void* ws, void* out, int N, int K,
+                                hipStream_t s) {
+  const size_t n = (size_t)N * (size_t)(K / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp4_dequant_kernel, dim3(blocks_for(n, kThreads)), dim3(kThreads), 0, s,
+                     static_cast<const uint32_t*>(wq), static_cast<const uint8_t*>(ws),
+                     static_cast<u32x4*>(out), N, K);
+  return hipGetLastError();
+}
+
+}  // namespace skg

@@ -1,0 +1,55 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skg {
+
+// Launch parameters of one split-K GEMM launch over at most 128 token rows.
+struct GemmParams {
+  const void* w;          // bf16 [N, K], or E2M1 bytes [N, K/2] (MXFP4)
+  const uint8_t* wscale;  // E8M0 codes [N, K/32] (MXFP4 only)
+  const void* x;          // bf16 [T, K]
+  void* c;                // bf16 [T, N]
+  float* part;            // FP32 partials [S, T, N] (S > 1)
+  uint32_t* cnt;          // one arrival counter per output tile (S > 1)
+  int T, N, K, S;
+  int ks;       // K / S: the K slice of one split rank
+  int kc;       // K elements of X staged in LDS at a time; divides ks
+  int nchunks;  // ks / kc
+};
+
+// A kernel configuration. One workgroup computes a TILE_N x T tile over one K
+// slice; its WK * WN waves split that slice WK ways along K (reduced through
+// LDS in wave order) and the tile WN ways along N; each wave owns RG groups
+// of 16 weight rows and keeps D load steps of weights in flight per group.
+struct Tactic {
+  int nt;       // 16-token MFMA tiles: T_pad = 16 * nt, 1..8
+  int rg;       // 16-row groups per wave
+  int wk;       // waves along K
+  int wn;       // waves along N
+  int d;        // weight load steps in flight per row group
+  int kc;       // K chunk staged in LDS
+  int tile_n;   // 16 * rg * wn
+  int threads;  // 64 * wk * wn
+  int lds;      // dynamic LDS bytes
+  int grid;     // workgroups = (N / tile_n) * split_k
+  int mx;       // 1 for MXFP4 weights
+};
+
+// Picks the configuration for a launch over T <= 128 rows; returns false if no
+// instantiated configuration fits (never for validated shapes).
+bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out);
+
+// Enqueues one launch (T <= 128). Returns the launch's hipError_t.
+hipError_t launch_gemm(const Tactic& tac, const GemmParams& p, hipStream_t stream);
+
+// Test and helper kernels (bit-exact checks of the device helpers).
+hipError_t launch_pack_bf16(const float* in, uint32_t* out, size_t n_pairs, hipStream_t s);
+hipError_t launch_pack_e4m3(const float* in, uint32_t* out, size_t n_quads, hipStream_t s);
+hipError_t launch_wave_sum(const float* in, float* out, size_t n_waves, hipStream_t s);
+hipError_t launch_mxfp4_dequant(const void* wq, const void* ws, void* out, int N, int K,
+                                hipStream_t s);
+
+}  // namespace skg

@@ -1,0 +1,106 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, and its host-side argument checks and tactic choice behave as the
+header states. No call here reaches the GPU (every call below is rejected, or
+has nothing to do, before any HIP runtime call)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import split_reduction_amd as sk
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "skgemm.h")
+
+
+def _ensure_built():
+    if not os.path.exists(sk.LIB_PATH):
+        from split_reduction_amd import build
+
+        build.build()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"SKGEMM_API\s+[\w\s\*]+?\b(skgemm_\w+)\s*\(", text)
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_symbols())
+    for must in ("skgemm_bf16", "skgemm_mxfp4", "skgemm_reserve", "skgemm_mxfp4_dequant",
+                 "skgemm_pack_bf16", "skgemm_pack_e4m3", "skgemm_wave_sum", "skgemm_tactic_for",
+                 "skgemm_strerror", "skgemm_last_hip_error", "skgemm_release"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    _ensure_built()
+    lib = ctypes.CDLL(sk.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", sk.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (skgemm_\w+)", out))
+    assert set(declared_symbols()) <= exported
+    # nothing else of ours leaks out of the library
+    assert {s for s in exported if s.startswith("skgemm")} == set(declared_symbols())
+
+
+def test_argument_checks_before_any_device_work():
+    _ensure_built()
+    lib = sk.lib()
+    a = 1 << 20  # a 16-byte aligned fake address: the checks below never dereference it
+    # split_k outside {1,2,4,8}
+    assert lib.skgemm_bf16(a, a, a, 1, 16, 96, 3, None) == sk.SKGEMM_EINVAL
+    # negative sizes
+    assert lib.skgemm_bf16(a, a, a, -1, 16, 64, 1, None) == sk.SKGEMM_EINVAL
+    # N not a multiple of 16, K not a multiple of 32*split_k
+    assert lib.skgemm_bf16(a, a, a, 1, 24, 64, 1, None) == sk.SKGEMM_ESHAPE
+    assert lib.skgemm_bf16(a, a, a, 1, 16, 96, 2, None) == sk.SKGEMM_ESHAPE
+    # MXFP4 needs K % (128 * split_k) == 0
+    assert lib.skgemm_mxfp4(a, a, a, a, 1, 16, 256, 4, None) == sk.SKGEMM_ESHAPE
+    # null and misaligned pointers
+    assert lib.skgemm_bf16(None, a, a, 1, 16, 64, 1, None) == sk.SKGEMM_EINVAL
+    assert lib.skgemm_bf16(a + 8, a, a, 1, 16, 64, 1, None) == sk.SKGEMM_EALIGN
+    assert lib.skgemm_mxfp4(a, None, a, a, 1, 16, 128, 1, None) == sk.SKGEMM_EINVAL
+    # size limits
+    assert lib.skgemm_bf16(a, a, a, 1, 1 << 19, 64, 1, None) == sk.SKGEMM_ESHAPE
+    # empty work: nothing enqueued, success, pointers not needed
+    assert lib.skgemm_bf16(None, None, None, 0, 16, 64, 1, None) == sk.SKGEMM_OK
+    assert lib.skgemm_bf16(None, None, None, 4, 0, 64, 1, None) == sk.SKGEMM_OK
+    assert lib.skgemm_pack_bf16(None, None, 0, None) == sk.SKGEMM_OK
+    assert lib.skgemm_wave_sum(a, None, 1, None) == sk.SKGEMM_EINVAL
+    assert lib.skgemm_mxfp4_dequant(a, a, a, 16, 48, None) == sk.SKGEMM_ESHAPE
+
+
+def test_strerror_covers_every_code():
+    _ensure_built()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert sk.strerror(code) and "unknown" not in sk.strerror(code)
+    assert "unknown" in sk.strerror(-99)
+
+
+@pytest.mark.parametrize("T,N,K,S,mx", [
+    (1, 1024, 1024, 4, False),
+    (8, 2048, 7168, 4, False),
+    (32, 18432, 7168, 8, False),
+    (16, 4096, 7168, 4, True),
+    (24, 16384, 16384, 4, False),
+    (128, 16384, 16384, 2, False),
+    (300, 256, 1024, 1, False),
+])
+def test_tactics_cover_the_workloads(T, N, K, S, mx):
+    _ensure_built()
+    t = sk.skgemm_tactic_for(T, N, K, S, mx)
+    assert t["nt"] == min((min(T, 128) + 15) // 16, 8)
+    assert N % t["tile_n"] == 0
+    assert t["grid"] == (N // t["tile_n"]) * S
+    assert (K // S) % t["kc"] == 0
+    assert t["lds"] <= 64 * 1024
+    assert t["token_blocks"] == (T + 127) // 128
+    step = 128 if mx else 32
+    assert t["kc"] % step == 0
+    assert 16 * t["nt"] * t["kc"] * 2 <= 64 * 1024

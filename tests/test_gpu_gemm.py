@@ -1,0 +1,225 @@
+"""GPU parity of the split-K GEMM against the fp64 oracle.
+
+Every case goes through the C ABI (``split_reduction_amd`` binding). The
+acceptance bound is |C - ref| <= 2^-7 |ref| + 1e-3 sqrt(K) rms(ref), element
+by element; exact special cases (integer operands, identity, one-hot rows)
+must match bit for bit.
+"""
+
+import numpy as np
+import pytest
+
+import split_reduction_amd as sk
+from oracle import formats as F
+from oracle import gemm as G
+from tests.gpu_util import (DEV, assert_parity, bf16_bits, empty_bf16, log, run_bf16, run_mxfp4,
+                            to_dev_bf16, to_dev_u8, torch)
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+# (T, N, K, split_k): shapes chosen to reach every instantiated workgroup
+# shape (tile 16 / 32 / 64 and the X-sharing tile), ragged T, several LDS
+# chunks per K slice, uneven step counts per wave, T above one 128-row block,
+# and K = 0.
+BF16_CASES = [
+    (1, 1024, 1024, 4),
+    (3, 4096, 512, 4),
+    (24, 8192, 512, 4),
+    (40, 8192, 1024, 8),
+    (64, 8192, 512, 4),
+    (100, 8192, 512, 4),
+    (128, 2048, 2048, 1),
+    (17, 256, 4096, 2),
+    (128, 512, 8192, 2),
+    (5, 160, 96, 1),
+    (9, 48, 192, 2),
+    (200, 96, 256, 2),
+    (2, 64, 0, 1),
+]
+
+
+@pytest.mark.parametrize("T,N,K,S", BF16_CASES)
+def test_bf16_parity_small(T, N, K, S):
+    log(f"bf16 parity T={T} N={N} K={K} S={S} tactic={sk.skgemm_tactic_for(T, N, K, S)}")
+    x, w = workloads.small_bf16_case(T, K, N, seed=1000 + T + N + K + S)
+    c = run_bf16(x, w, S)
+    ref = G.gemm_bf16_ref(x, w)
+    if K == 0:
+        assert np.all(F.bf16_bits_to_f64(c) == 0.0)
+        return
+    assert_parity(c, ref, K, f"T={T} N={N} K={K} S={S}")
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 8])
+@pytest.mark.parametrize("T", [1, 5, 16, 33, 128])
+def test_bf16_integer_operands_bit_exact(T, S):
+    N, K = 512, 1024
+    log(f"bf16 integer exact T={T} S={S}")
+    x, w = workloads.integer_bf16_case(T, K, N, seed=2000 + T * 10 + S)
+    c = run_bf16(x, w, S)
+    exact = G.gemm_bf16_ref(x, w)  # integers below 2^24: every FP32 order is exact
+    assert np.max(np.abs(exact)) < 2**24
+    ref = F.f32_to_bf16_rne(exact.astype(np.float32))
+    assert np.array_equal(c, ref)
+
+
+def test_bf16_identity_and_permutation_bit_exact():
+    rng = np.random.default_rng(31)
+    T, K = 7, 512
+    x = workloads.to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+    log("bf16 identity")
+    eye = workloads.to_bf16_bits(np.eye(K, dtype=np.float32))
+    c = run_bf16(x, eye, 2)
+    assert np.array_equal(F.bf16_bits_to_f64(c), F.bf16_bits_to_f64(x))
+    log("bf16 one-hot permutation")
+    N = 256
+    perm = rng.permutation(K)[:N]
+    w = np.zeros((N, K), dtype=np.float32)
+    w[np.arange(N), perm] = 1.0
+    c = run_bf16(x, workloads.to_bf16_bits(w), 4)
+    assert np.array_equal(F.bf16_bits_to_f64(c), F.bf16_bits_to_f64(x)[:, perm])
+
+
+def test_bf16_repeatable_bits():
+    w = workloads.WORKLOADS["bf16_t8_k7168_n2048"]
+    x = workloads.gen_x(w)
+    wb = workloads.gen_w_bf16(w)
+    log("bf16 determinism on the T=8 K=7168 N=2048 workload")
+    W = to_dev_bf16(wb)
+    first = run_bf16(x, None, w.split_k, W=W)
+    for _ in range(3):
+        assert np.array_equal(run_bf16(x, None, w.split_k, W=W), first)
+
+
+def test_bf16_writes_only_c_once():
+    T, N, K, S = 5, 320, 1024, 4
+    log("bf16 write bounds")
+    x, w = workloads.small_bf16_case(T, K, N, seed=41)
+    t = torch()
+    sentinel = 0x7FC1  # a NaN pattern the kernel never produces from finite inputs
+    buf = t.full((T + 3, N), sentinel, dtype=t.int16, device=DEV).view(t.bfloat16)
+    C = buf[:T]
+    sk.skgemm_bf16(to_dev_bf16(w), to_dev_bf16(x), C, T, N, K, S)
+    t.cuda.synchronize()
+    allb = bf16_bits(buf)
+    assert np.all(allb[T:] == sentinel)
+    assert not np.any(allb[:T] == sentinel)
+    assert_parity(allb[:T], G.gemm_bf16_ref(x, w), K, "bounded write")
+
+
+def test_bf16_rejects_bad_arguments_without_touching_c():
+    t = torch()
+    log("bf16 argument errors")
+    W = t.zeros((32, 96), dtype=t.bfloat16, device=DEV)
+    X = t.zeros((2, 96), dtype=t.bfloat16, device=DEV)
+    C = t.full((2, 32), 7, dtype=t.int16, device=DEV).view(t.bfloat16)
+    for args, code in [((2, 32, 96, 2), sk.SKGEMM_ESHAPE), ((2, 32, 96, 3), sk.SKGEMM_EINVAL),
+                       ((2, 30, 96, 1), sk.SKGEMM_ESHAPE)]:
+        with pytest.raises(sk.SkgemmError) as e:
+            sk.skgemm_bf16(W, X, C, *args)
+        assert e.value.code == code
+    with pytest.raises(sk.SkgemmError) as e:
+        sk.skgemm_bf16(W.data_ptr() + 2, X, C, 2, 32, 96, 1)
+    assert e.value.code == sk.SKGEMM_EALIGN
+    t.cuda.synchronize()
+    assert np.all(bf16_bits(C) == 7)
+
+
+def test_bf16_two_streams():
+    t = torch()
+    w = workloads.WORKLOADS["bf16_t8_k7168_n2048"]
+    x = workloads.gen_x(w)
+    wb = workloads.gen_w_bf16(w)
+    ref = G.gemm_bf16_ref(x, wb)
+    log("bf16 on two streams at once")
+    W, X = to_dev_bf16(wb), to_dev_bf16(x)
+    s1, s2 = t.cuda.Stream(), t.cuda.Stream()
+    outs = []
+    t.cuda.synchronize()
+    for s in (s1, s2):
+        with t.cuda.stream(s):
+            C = empty_bf16(w.T, w.N)
+            for _ in range(4):
+                sk.skgemm_bf16(W, X, C, w.T, w.N, w.K, w.split_k)
+            outs.append(C)
+    t.cuda.synchronize()
+    for C in outs:
+        assert_parity(bf16_bits(C), ref, w.K, "two streams")
+
+
+# ---------------------------------------------------------------- MXFP4 ----
+
+MX_CASES = [
+    (1, 256, 512, 1),
+    (3, 4096, 512, 4),
+    (16, 1024, 1024, 2),
+    (40, 2048, 1024, 4),
+    (128, 512, 2048, 2),
+    (130, 64, 256, 1),
+]
+
+
+@pytest.mark.parametrize("T,N,K,S", MX_CASES)
+def test_mxfp4_parity_small(T, N, K, S):
+    log(f"mxfp4 parity T={T} N={N} K={K} S={S} tactic={sk.skgemm_tactic_for(T, N, K, S, True)}")
+    x, wq, ws = workloads.small_mxfp4_case(T, K, N, seed=3000 + T + N + K + S)
+    c = run_mxfp4(x, wq, ws, S)
+    assert_parity(c, G.gemm_mxfp4_ref(x, wq, ws), K, f"mxfp4 T={T} N={N} K={K} S={S}")
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_mxfp4_integer_operands_bit_exact(S):
+    T, N, K = 20, 256, 1024
+    log(f"mxfp4 integer exact S={S}")
+    rng = np.random.default_rng(50 + S)
+    x = workloads.to_bf16_bits(rng.integers(-3, 4, size=(T, K)).astype(np.float32))
+    wq = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    ws = np.full((N, K // 32), 127, dtype=np.uint8)  # scale 1: weights in {0, +-0.5, ..., +-6}
+    c = run_mxfp4(x, wq, ws, S)
+    exact = G.gemm_mxfp4_ref(x, wq, ws)  # multiples of 0.5 below 2^22: exact in FP32
+    assert np.max(np.abs(exact)) < 2**22
+    assert np.array_equal(c, F.f32_to_bf16_rne(exact.astype(np.float32)))
+
+
+# ------------------------------------------------------ full workloads -----
+
+
+@pytest.mark.parametrize("name", ["bf16_t1_k1024_n1024", "bf16_t8_k7168_n2048", "bf16_t32_k7168_n18432"])
+def test_bf16_workload_full_parity(name):
+    w = workloads.WORKLOADS[name]
+    log(f"workload {name} tactic={sk.skgemm_tactic_for(w.T, w.N, w.K, w.split_k)}")
+    x = workloads.gen_x(w)
+    wb = workloads.gen_w_bf16(w)
+    c = run_bf16(x, wb, w.split_k)
+    assert_parity(c, G.gemm_bf16_ref(x, wb), w.K, name)
+
+
+def test_mxfp4_workload_full_parity():
+    w = workloads.WORKLOADS["mxfp4_t16_k7168_n4096"]
+    log(f"workload {w.name} tactic={sk.skgemm_tactic_for(w.T, w.N, w.K, w.split_k, True)}")
+    x = workloads.gen_x(w)
+    wq, ws = workloads.gen_w_mxfp4(w)
+    c = run_mxfp4(x, wq, ws, w.split_k)
+    assert_parity(c, G.gemm_mxfp4_ref(x, wq, ws), w.K, w.name)
+
+
+@pytest.fixture(scope="module")
+def sweep_weights():
+    w = workloads.sweep_workload(1)
+    log("generating the K = N = 16384 sweep weights")
+    wb = workloads.gen_w_bf16(w)
+    return wb, to_dev_bf16(wb)
+
+
+@pytest.mark.parametrize("T", list(workloads.SWEEP_T))
+def test_bf16_sweep_sampled_parity(T, sweep_weights):
+    wb, W = sweep_weights
+    w = workloads.sweep_workload(T)
+    log(f"sweep T={T} S={w.split_k} tactic={sk.skgemm_tactic_for(T, w.N, w.K, w.split_k)}")
+    x = workloads.gen_x(w)
+    c = run_bf16(x, None, w.split_k, W=W)
+    rows = np.random.default_rng(60 + T).choice(w.N, size=1024, replace=False)
+    ref = G.gemm_bf16_ref(x, wb[rows])
+    # the rms of the sampled columns estimates the full output's rms
+    assert_parity(c[:, rows], ref, w.K, f"sweep T={T} (1024 sampled features)")
