@@ -1,0 +1,373 @@
+"""Benchmark of the split-K decode GEMM on one MI355X.
+
+Prints ONE JSON line. The headline workload is bf16 T=8, K=7168, N=2048,
+split_k=4 (W ~ N(0, 0.02^2), X ~ N(0, 1)); one step is one skgemm_bf16 call
+(the whole hot path: weight stream, X staging, MFMA, LDS and split-K
+reductions, bf16 epilogue). The metric is the weight-stream rate: weight bytes
+per step / step time, in TB/s, and its fraction of the 8 TB/s HBM3E peak.
+
+Timing protocol:
+* inputs are resident in HBM before the timed region; R copies of the weights
+  (R * weight bytes >= 1 GiB, four times the 256 MiB last-level cache) are
+  rotated so every step streams weights that are not cache-resident;
+* W untimed warmup steps run eagerly, then exactly K steps are replayed from
+  one HIP graph (no host launch gaps), bracketed by synchronisations and
+  timed with HIP events recorded on the stream the kernels run on;
+* the same protocol without rotation gives the labelled cache-resident rate.
+
+The other workloads (bf16 T=1 K=1024 N=1024; bf16 T=32 K=7168 N=18432 with
+outlier channels; MXFP4 T=16 K=7168 N=4096; the K = N = 16384 bf16 sweep over
+T) are timed the same way and reported under "workloads". The cpu_baseline
+leg times the fp64 oracle on the host on the headline workload.
+
+``--trace-summary DIR`` reads a rocprofv3 kernel trace written under DIR and
+prints per-workload kernel durations (matched by kernel name and grid size).
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+ROTATE_BYTES = 1 << 30
+HEADLINE = "bf16_t8_k7168_n2048"
+KERNEL_SOURCES = ["split_reduction_amd/csrc/gemm.hip", "split_reduction_amd/csrc/device/types.h",
+                  "split_reduction_amd/csrc/device/pack.h", "split_reduction_amd/csrc/device/mxfp4.h",
+                  "split_reduction_amd/csrc/device/mfma.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+
+class Case:
+    """Device-resident operands of one workload at one T, with rotated weights."""
+
+    def __init__(self, wl: workloads.Workload, host_w=None):
+        import torch
+
+        self.wl = wl
+        self.torch = torch
+        dev = "cuda:0"
+        x = workloads.gen_x(wl)
+        self.x_bits = x
+        self.X = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.C = torch.empty((wl.T, wl.N), dtype=torch.bfloat16, device=dev)
+        if wl.kind == "mxfp4":
+            wq, ws = host_w if host_w is not None else workloads.gen_w_mxfp4(wl)
+            base = (torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev))
+        else:
+            wb = host_w if host_w is not None else workloads.gen_w_bf16(wl)
+            base = (torch.from_numpy(wb.view(np.int16)).to(dev).view(torch.bfloat16),)
+        self.copies = max(1, math.ceil(ROTATE_BYTES / wl.weight_bytes()))
+        self.weights = [base] + [tuple(t.clone() for t in base) for _ in range(self.copies - 1)]
+
+    def launch(self, i: int, stream):
+        import split_reduction_amd as sk
+
+        wl = self.wl
+        w = self.weights[i % len(self.weights)]
+        if wl.kind == "mxfp4":
+            sk.skgemm_mxfp4(w[0], w[1], self.X, self.C, wl.T, wl.N, wl.K, wl.split_k, stream)
+        else:
+            sk.skgemm_bf16(w[0], self.X, self.C, wl.T, wl.N, wl.K, wl.split_k, stream)
+
+    def time(self, steps: int, warmup: int, rotate: bool = True) -> dict:
+        torch = self.torch
+        import split_reduction_amd as sk
+
+        wl = self.wl
+        stream = torch.cuda.Stream()
+        sk.skgemm_reserve(wl.T, wl.N, wl.split_k, stream)
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                self.launch(i if rotate else 0, stream)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                self.launch(i if rotate else 0, stream)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()  # the graph's own first replay (uploads it); untimed
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):  # replay() launches on the current stream
+            start.record(stream)
+            g.replay()
+            end.record(stream)
+        end.synchronize()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end)
+        del g
+        t_s = ms * 1e-3 / steps
+        return {
+            "t_us": t_s * 1e6,
+            "weight_TBps": wl.weight_bytes() / t_s / 1e12,
+            "algo_GBps": self.algo_bytes() / t_s / 1e9,
+            "TFLOPs": wl.flops() / t_s / 1e12,
+        }
+
+    def algo_bytes(self) -> int:
+        """Compulsory bytes of one call: weights + X + C."""
+        wl = self.wl
+        return wl.weight_bytes() + 2 * wl.T * wl.K + 2 * wl.T * wl.N
+
+
+def run_workload(wl, steps, warmup, host_w=None) -> dict:
+    import split_reduction_amd as sk
+
+    case = Case(wl, host_w)
+    cold = case.time(steps, warmup, rotate=True)
+    hot = case.time(steps, warmup, rotate=False)
+    tac = sk.skgemm_tactic_for(wl.T, wl.N, wl.K, wl.split_k, wl.kind == "mxfp4")
+    out = {
+        "workload": wl.name, "kind": wl.kind, "T": wl.T, "K": wl.K, "N": wl.N,
+        "split_k": wl.split_k, "weight_bytes": wl.weight_bytes(), "flops": wl.flops(),
+        "rotated_copies": case.copies,
+        "t_us": round(cold["t_us"], 3),
+        "weight_TBps": round(cold["weight_TBps"], 4),
+        "frac_hbm_peak": round(cold["weight_TBps"] * 1000 / HBM_PEAK_GBS, 4),
+        "TFLOPs": round(cold["TFLOPs"], 3),
+        "frac_mfma_peak": round(cold["TFLOPs"] / BF16_MFMA_PEAK_TFLOPS, 5),
+        "hot_t_us": round(hot["t_us"], 3),
+        "hot_weight_TBps": round(hot["weight_TBps"], 4),
+        "tactic": {k: tac[k] for k in ("nt", "rg", "wk", "wn", "d", "kc", "tile_n", "grid")},
+        "_algo_bytes": case.algo_bytes(),
+    }
+    del case
+    import torch
+
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on the host cores
+# ---------------------------------------------------------------------------
+
+
+def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
+    from oracle import gemm
+
+    x = workloads.gen_x(wl)
+    wb = workloads.gen_w_bf16(wl)
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # threadpoolctl missing: report the visible CPUs
+        cores = os.cpu_count() or 1
+    gemm.gemm_bf16_ref(x, wb)  # first call outside the timing
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        gemm.gemm_bf16_ref(x, wb)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per = el / n
+    return {
+        "value": round(wl.weight_bytes() / per / 1e12, 6),
+        "unit": "TB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"the whole {wl.name} workload (bf16->fp64 conversion and fp64 numpy GEMM), "
+                   f"{n} calls in {el:.1f} s, {per * 1e3:.2f} ms per call"),
+    }
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 trace summary
+# ---------------------------------------------------------------------------
+
+
+def trace_summary(path: str, steps: int, warmup: int) -> None:
+    """Per-kernel durations from a rocprofv3 kernel trace of this script.
+
+    Dispatches are taken in time order and cut into runs of the same kernel
+    and grid. The first run is the headline workload: per timing pass, W eager
+    warmup launches, the graph's untimed first replay and its timed replay of
+    K launches; one cold (rotated weights) pass, then one cache-resident pass.
+    """
+    import csv
+
+    files = glob.glob(os.path.join(path, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_trace.csv under {path}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    rows = [r for r in rows if "splitk_" in r.get("Kernel_Name", "")]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    segs = []
+    for r in rows:
+        key = (r["Kernel_Name"], r.get("Grid_Size", r.get("Grid_Size_X", "?")))
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+        if segs and segs[-1][0] == key:
+            segs[-1][1].append(dur)
+        else:
+            segs.append((key, [dur]))
+    print("run  calls   avg(us)   med(us)   min(us)     grid  kernel")
+    for i, ((name, grid), durs) in enumerate(segs):
+        d = np.array(durs)
+        short = name.replace("void skg::", "").replace("(skg::GemmParams)", "")
+        print(f"{i:3d} {len(d):6d} {d.mean():9.3f} {np.median(d):9.3f} {d.min():9.3f} {grid:>8}  {short}")
+    if segs:
+        d = np.array(segs[0][1])
+        per_pass = warmup + 2 * steps
+        if len(d) >= 2 * per_pass:
+            cold = d[warmup + steps:per_pass]
+            hot = d[per_pass + warmup + steps:2 * per_pass]
+            print(f"headline cold timed replay: {len(cold)} launches, avg {cold.mean():.3f} us, "
+                  f"median {np.median(cold):.3f} us")
+            print(f"headline cache-resident timed replay: {len(hot)} launches, avg {hot.mean():.3f} us")
+
+
+# ---------------------------------------------------------------------------
+
+
+def load_traffic(headline_name: str):
+    """HBM bytes per launch measured by rocprofv3 counters, if they were taken
+    on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{headline_name}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-summary", metavar="DIR", help="summarise a rocprofv3 kernel trace and exit")
+    args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.steps, args.warmup)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        raise SystemExit(2)
+
+    import torch
+
+    import split_reduction_amd as sk
+
+    if not os.path.exists(sk.LIB_PATH):
+        from split_reduction_amd import build
+
+        build.build()
+    sk.lib()
+    torch.cuda.init()
+
+    head = workloads.WORKLOADS[HEADLINE]
+    log(f"headline {head.name}")
+    h = run_workload(head, args.steps, args.warmup)
+    log(json.dumps({k: v for k, v in h.items() if not k.startswith("_")}))
+
+    extra = []
+    if not args.only_headline:
+        steps = max(20, args.steps // 2)
+        warm = max(3, args.warmup // 2)
+        for name in ("bf16_t1_k1024_n1024", "bf16_t32_k7168_n18432", "mxfp4_t16_k7168_n4096"):
+            log(f"workload {name}")
+            r = run_workload(workloads.WORKLOADS[name], steps, warm)
+            log(json.dumps({k: v for k, v in r.items() if not k.startswith("_")}))
+            extra.append(r)
+        log("sweep weights K = N = 16384")
+        sw = workloads.sweep_workload(1)
+        wsweep = workloads.gen_w_bf16(sw)
+        for T in workloads.SWEEP_T:
+            r = run_workload(workloads.sweep_workload(T), steps, warm, host_w=wsweep)
+            log(json.dumps({k: v for k, v in r.items() if not k.startswith("_")}))
+            extra.append(r)
+        del wsweep
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(head)
+
+    t_s = h["t_us"] * 1e-6
+    achieved = h["_algo_bytes"] / t_s / 1e9
+    line = {
+        "metric": "weight-stream HBM TB/s (% of peak) + TFLOP/s, split-K decode GEMM, 1 GPU",
+        "value": h["weight_TBps"],
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["t_us"] * 1e-3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "frac_hbm_peak": h["frac_hbm_peak"],
+        "TFLOPs": h["TFLOPs"],
+        "config": {
+            "workload": head.name, "T": head.T, "K": head.K, "N": head.N,
+            "split_k": head.split_k, "weights": "bf16 N(0,0.02^2)", "activations": "bf16 N(0,1)",
+            "cache": f"cold: {h['rotated_copies']} rotated weight copies (>= 1 GiB)",
+            "timing": "HIP graph of exactly `steps` launches, HIP events on the launch stream",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(head.name),
+        },
+        "cpu_baseline": cpu,
+        "hot_cache": {"t_us": h["hot_t_us"], "weight_TBps": h["hot_weight_TBps"]},
+        "tactic": h["tactic"],
+        "workloads": [{k: v for k, v in r.items() if not k.startswith("_")} for r in extra],
+        "kernel_source_sha": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

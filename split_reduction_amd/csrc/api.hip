@@ -9,7 +9,7 @@
 #include <mutex>
 #include <utility>
 
-#include "../../include/skgemm.h"
+#include "skgemm.h"
 #include "skgemm_internal.h"
 
 namespace {
@@ -220,11 +220,11 @@ SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int mxfp4, ch
   const int blocks = (T + kTokenBlock - 1) / kTokenBlock;
   if (buf != nullptr && buf_len > 0) {
     snprintf(buf, buf_len,
-             "{\"nt\": %d, \"rg\": %d, \"wk\": %d, \"wn\": %d, \"d\": %d, \"kc\": %d, "
+             "{\"nt\": %d, \"rg\": %d, \"wk\": %d, \"wn\": %d, \"d\": %d, \"c\": %d, \"kc\": %d, "
              "\"tile_n\": %d, \"threads\": %d, \"lds\": %d, \"grid\": %d, \"split_k\": %d, "
-             "\"token_blocks\": %d, \"mxfp4\": %d}",
-             t.nt, t.rg, t.wk, t.wn, t.d, t.kc, t.tile_n, t.threads, t.lds, t.grid, split_k,
-             blocks, t.mx);
+             "\"token_blocks\": %d, \"mxfp4\": %d, \"kind\": \"%s\"}",
+             t.nt, t.rg, t.wk, t.wn, t.d, t.c, t.kc, t.tile_n, t.threads, t.lds, t.grid, split_k,
+             blocks, t.mx, t.kind == 1 ? "stream" : "tiled");
   }
   return SKGEMM_OK;
 }

@@ -29,6 +29,11 @@ constexpr uint32_t kOOB = 0x80000000u;
 // Cache-policy bits of a buffer access on gfx950: bit 1 is NT (streaming).
 constexpr int kPolicyDefault = 0;
 constexpr int kPolicyStream = 2;
+// SC1: device-scope coherent access. Such a store is written through to the
+// level all XCDs share and such a load does not hit a non-coherent copy, so
+// they need no cache-wide writeback or invalidate around them (the bits the
+// compiler itself emits for relaxed device-scope atomic loads and stores).
+constexpr int kPolicyDeviceCoherent = 16;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
@@ -56,5 +61,17 @@ __device__ __forceinline__ void st8_if(bool ok, u32x2 v, rsrc_t r, uint32_t off)
 __device__ __forceinline__ void st4_if(bool ok, uint32_t v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, ok ? off : kOOB, 0, kPolicyDefault);
 }
+
+// Device-scope coherent 16-byte store / load (predicated like the above).
+__device__ __forceinline__ void st16_coherent_if(bool ok, u32x4 v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, ok ? off : kOOB, 0, kPolicyDeviceCoherent);
+}
+__device__ __forceinline__ u32x4 ld16_coherent_if(bool ok, rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, ok ? off : kOOB, 0, kPolicyDeviceCoherent);
+}
+
+// Waits until every vector memory access this wave issued has completed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace skg

@@ -35,6 +35,8 @@
 //    and e8m0_f32). The activations are staged with the same K permutation,
 //    which leaves the contraction unchanged.
 
+#include <stdlib.h>
+
 #include "device/mfma.h"
 #include "device/mxfp4.h"
 #include "device/pack.h"
@@ -55,14 +57,14 @@ __device__ __forceinline__ void lds_write16(uint8_t* smem, int slot, u32x4 v) {
 
 }  // namespace
 
-template <int NT, int RG, int WK, int WN, int D, bool MX>
+template <int NT, int RG, int WK, int WN, int D, int C, bool MX>
 __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p) {
   constexpr int THREADS = 64 * WK * WN;
   constexpr int TILE_N = 16 * RG * WN;
-  constexpr int STEP_K = MX ? 128 : 32;  // K elements of one 16-byte lane load, per row
-  constexpr int SUB = MX ? 4 : 1;        // MFMA K-steps per load step
-  constexpr int TPAD = 16 * NT;
-  constexpr int XBATCH = 4;              // staging loads issued before their LDS writes
+  constexpr int LOADS = MX ? 1 : C;          // 16-byte weight loads per row group per step
+  constexpr int SUBS = MX ? 4 : C;           // MFMA K-steps per load step
+  constexpr int STEP_K = MX ? 128 : 32 * C;  // K elements of one load step
+  constexpr int XBATCH = 4;                  // staging loads issued before their LDS writes
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t s_last;
@@ -100,6 +102,12 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
     row_off[rg] = row * wrow_bytes;
     srow_off[rg] = row * (uint32_t)(K / 32);
   }
+  // Byte offset, within a weight row, of this lane's first piece of a step
+  // starting at K element kel: bf16 pieces c cover K elements
+  // kel + 8C*g + 8c .. +7; an MXFP4 lane covers kel + 32g .. +31.
+  auto w_lane_off = [&](int kel) -> uint32_t {
+    return MX ? (uint32_t)(kel / 2 + 16 * g) : (uint32_t)(kel * 2 + 16 * C * g);
+  };
 
   f32x4 acc[RG][NT];
 #pragma unroll
@@ -107,85 +115,89 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[rg][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ring[D][RG];
+  u32x4 ring[D][RG][LOADS];
   uint32_t sring[D][RG];
+
+  // Activation operand slot of (load step j, MFMA sub-step s, lane K block
+  // gg, token t) in the compact LDS tile: only real tokens are stored.
+  auto x_slot = [&](int j, int s, int gg, int t) -> int { return ((j * SUBS + s) * 4 + gg) * T + t; };
 
   for (int c = 0; c < p.nchunks; ++c) {
     const int kc0 = kbase + c * p.kc;  // first K element of the chunk
     const int cs = p.kc / STEP_K;      // load steps in the chunk
     const int n_i = (cs - wk + WK - 1) / WK;  // this wave's steps: j = wk + WK * i
 
-    // Weight prologue: D load steps, issued before the staging below so the
-    // X loads' latency hides under the weight loads'.
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-      const bool ok = s < n_i;
-      const int kel = kc0 + (wk + WK * s) * STEP_K;
+    auto issue = [&](int slot_s, int i) {
+      const bool ok = i < n_i;
+      const int kel = kc0 + (wk + WK * i) * STEP_K;
+      const uint32_t lo = w_lane_off(kel);
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
-        if constexpr (MX) {
-          ring[s][rg] = ld16_if<kPolicyStream>(ok, wr, row_off[rg] + kel / 2 + 16 * g);
-          sring[s][rg] = ld1_if<kPolicyStream>(ok, sr, srow_off[rg] + kel / 32 + g);
-        } else {
-          ring[s][rg] = ld16_if<kPolicyStream>(ok, wr, row_off[rg] + kel * 2 + 16 * g);
-        }
+#pragma unroll
+        for (int l = 0; l < LOADS; ++l) ring[slot_s][rg][l] = ld16_if(ok, wr, row_off[rg] + lo + 16 * l);
+        if constexpr (MX) sring[slot_s][rg] = ld1_if(ok, sr, srow_off[rg] + kel / 32 + g);
       }
-    }
+    };
+
+    // Weight prologue first: the X staging below hides under its latency.
+#pragma unroll
+    for (int s = 0; s < D; ++s) issue(s, s);
 
     if (c > 0) __syncthreads();  // every wave is done reading the previous chunk
 
-    // Stage X[0:TPAD, kc0 : kc0 + kc) into LDS in MFMA B-operand order.
-    // Piece (t, q) = 8 bf16 at chunk-local K 8q of row t; consecutive threads
-    // take consecutive rows, so a wave writes 1 KiB of LDS contiguously.
+    // Stage X[0:T, kc0 : kc0 + kc) in LDS. Consecutive threads take
+    // consecutive tokens of one 8-element piece, so writes are contiguous.
     {
-      const int pieces = TPAD * (p.kc / 8);
+      const int pieces = T * (p.kc / 8);
       for (int p0 = tid; p0 < pieces; p0 += THREADS * XBATCH) {
         u32x4 v[XBATCH];
 #pragma unroll
         for (int b = 0; b < XBATCH; ++b) {
           const int pc = p0 + b * THREADS;
-          const int t = pc % TPAD;
-          const int k = (pc / TPAD) * 8;
-          const bool ok = (pc < pieces) && (t < T);
-          v[b] = ld16_if(ok, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(kc0 + k)) * 2u);
+          const int t = pc % T;
+          const int k = (pc / T) * 8;
+          v[b] = ld16_if(pc < pieces, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(kc0 + k)) * 2u);
         }
 #pragma unroll
         for (int b = 0; b < XBATCH; ++b) {
           const int pc = p0 + b * THREADS;
           if (pc < pieces) {
-            const int t = pc % TPAD;
-            const int k = (pc / TPAD) * 8;
-            int slot;
+            const int t = pc % T;
+            const int k = (pc / T) * 8;
+            int j, s, gg;
             if constexpr (MX) {
-              const int m = k / 128, gg = (k % 128) / 32, d = (k % 32) / 8;
-              slot = ((m * 4 + d) * NT + t / 16) * 64 + gg * 16 + (t % 16);
+              j = k / 128; gg = (k % 128) / 32; s = (k % 32) / 8;
             } else {
-              const int j = k / 32, gg = (k % 32) / 8;
-              slot = (j * NT + t / 16) * 64 + gg * 16 + (t % 16);
+              j = k / (32 * C); gg = (k % (32 * C)) / (8 * C); s = (k % (8 * C)) / 8;
             }
-            lds_write16(smem, slot, v[b]);
+            lds_write16(smem, x_slot(j, s, gg, t), v[b]);
           }
         }
       }
     }
     __syncthreads();
 
-    // One load step: RG weight operands against NT activation operands.
-    auto compute = [&](const u32x4 (&a)[RG], const uint32_t (&sc)[RG], int i) {
+    // One load step: RG weight operands per MFMA sub-step against NT
+    // activation operands (zero for tokens >= T).
+    auto compute = [&](const u32x4 (&a)[RG][LOADS], const uint32_t (&sc)[RG], int i) {
       const int j = wk + WK * i;  // chunk-local load step
 #pragma unroll
-      for (int sub = 0; sub < SUB; ++sub) {
+      for (int s = 0; s < SUBS; ++s) {
         bf16x8 b[NT];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
-          b[tt] = as_bf16x8(lds_read16(smem, ((j * SUB + sub) * NT + tt) * 64 + lane));
+        for (int tt = 0; tt < NT; ++tt) {
+          const int t = tt * 16 + li;
+          const bool ok = t < T;
+          const u32x4 v = lds_read16(smem, x_slot(j, s, g, ok ? t : 0));
+          b[tt] = as_bf16x8(ok ? v : u32x4{0u, 0u, 0u, 0u});
+        }
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
           bf16x8 af;
           if constexpr (MX) {
-            af = fp4x8_bf16(a[rg][sub], e8m0_f32(sc[rg]));
+            af = fp4x8_bf16(a[rg][0][s], e8m0_f32(sc[rg]));
           } else {
-            af = as_bf16x8(a[rg]);
+            af = as_bf16x8(a[rg][s]);
           }
 #pragma unroll
           for (int tt = 0; tt < NT; ++tt) acc[rg][tt] = mfma_bf16(af, b[tt], acc[rg][tt]);
@@ -193,30 +205,16 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
       }
     };
 
+    // Steady state: consume slot s, then refill the same registers with the
+    // step D ahead, so D - 1 steps stay in flight while one is multiplied and
+    // no register copies (which would wait for loads) are needed.
     int i0 = 0;
     for (; i0 + D <= n_i; i0 += D) {
 #pragma unroll
       for (int s = 0; s < D; ++s) {
-        u32x4 a[RG];
-        uint32_t sc[RG];
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-          a[rg] = ring[s][rg];
-          sc[rg] = sring[s][rg];
-        }
-        const int inext = i0 + s + D;
-        const bool ok = inext < n_i;
-        const int kel = kc0 + (wk + WK * inext) * STEP_K;
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-          if constexpr (MX) {
-            ring[s][rg] = ld16_if<kPolicyStream>(ok, wr, row_off[rg] + kel / 2 + 16 * g);
-            sring[s][rg] = ld1_if<kPolicyStream>(ok, sr, srow_off[rg] + kel / 32 + g);
-          } else {
-            ring[s][rg] = ld16_if<kPolicyStream>(ok, wr, row_off[rg] + kel * 2 + 16 * g);
-          }
-        }
-        compute(a, sc, i0 + s);
+        compute(ring[s], sring[s], i0 + s);
+        issue(s, i0 + s + D);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
@@ -271,6 +269,12 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
   }
 
   // ---- split-K hand-off across workgroups --------------------------------
+  // Partials are written with device-scope coherent stores (they bypass the
+  // non-coherent caches of this XCD), each wave waits for its stores to be
+  // acknowledged, and thread 0 then bumps the tile's arrival counter with a
+  // device-scope atomic. The last arriver reads the other ranks' partials
+  // with device-scope coherent loads. No cache-wide writeback or invalidate
+  // is needed.
   const rsrc_t pr = make_rsrc(p.part, (uint32_t)S * (uint32_t)T * (uint32_t)N * 4u);
   auto p_off = [&](int r, int rg, int tt) -> uint32_t {
     return (((uint32_t)r * (uint32_t)T + (uint32_t)(tt * 16 + li)) * (uint32_t)N +
@@ -280,21 +284,18 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
   for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
-      st16_if(in_t(tt), __builtin_bit_cast(u32x4, acc[rg][tt]), pr, p_off(rank, rg, tt));
-  // Every wave releases its own partial stores at agent scope before the
-  // workgroup barrier; thread 0's arrival then carries them to the last rank.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, acc[rg][tt]), pr, p_off(rank, rg, tt));
+  wait_vmem_all();
   __syncthreads();
   if (tid == 0) {
     const uint32_t old =
-        __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = (old == (uint32_t)(S - 1));
     if (last) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = last ? 1u : 0u;
   }
   __syncthreads();
   if (s_last == 0 || !owner) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   // The last rank to arrive sums the ranks' partials in rank order 0..S-1,
   // taking its own from registers, rounds once and stores C once.
@@ -303,14 +304,278 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) {
       const bool ok = in_t(tt);
-      f32x4 tot = (rank == 0) ? acc[rg][tt]
-                              : __builtin_bit_cast(f32x4, ld16_if(ok, pr, p_off(0, rg, tt)));
-      for (int r = 1; r < S; ++r) {
-        const f32x4 v = (r == rank) ? acc[rg][tt]
-                                    : __builtin_bit_cast(f32x4, ld16_if(ok, pr, p_off(r, rg, tt)));
-        tot += v;
+      f32x4 v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        if (r < S && r != rank)
+          v[r] = __builtin_bit_cast(f32x4, ld16_coherent_if(ok, pr, p_off(r, rg, tt)));
+      }
+      f32x4 tot = (rank == 0) ? acc[rg][tt] : v[0];
+#pragma unroll
+      for (int r = 1; r < 8; ++r) {
+        if (r < S) tot += (r == rank) ? acc[rg][tt] : v[r];
       }
       st8_if(ok, bf16_quad(tot), cr, c_off(rg, tt));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Persistent streaming kernel (16-row tiles, X staged once per workgroup)
+// ---------------------------------------------------------------------------
+//
+// grid = S * G workgroups of WK * WN waves; workgroup (gi, rank) owns K slice
+// `rank`. Its WN wave columns each own a list of 16-row tiles (column
+// gi*WN + wn takes tiles gi*WN + wn, + G*WN, ...); the WK waves of a column
+// split every tile's K slice (interleaved load steps). The workgroup stages
+// its X slice in LDS once, shared by all its waves; each wave then streams
+// the weight rows of all its tiles through one D-deep register ring that runs
+// on across tile boundaries, so neither the staging nor the load latency is
+// paid per tile. At a tile's end the WK waves' partial sums meet in LDS
+// (wave order, WK > 1 only) and the column's wave 0 writes the tile's FP32
+// partial (device-coherent) or, without a split, the bf16 output. The
+// hand-off is deferred to the end: one wait for all stores, then one counter
+// atomic per tile; the last rank to arrive on a tile sums the ranks'
+// partials in rank order and stores C. Waiting for stores mid-stream would
+// drain the ring (loads and stores share one counter and may complete out
+// of order relative to each other), which is why nothing is signalled early.
+// With WK > 1 the host uses WN = 1, so every wave meets the same barriers.
+template <int NT, int WK, int WN, int D, int C, bool MX>
+__global__ __launch_bounds__(64 * WK * WN) void splitk_stream_kernel(GemmParams p) {
+  constexpr int THREADS = 64 * WK * WN;
+  constexpr int LOADS = MX ? 1 : C;
+  constexpr int SUBS = MX ? 4 : C;
+  constexpr int STEP_K = MX ? 128 : 32 * C;
+  constexpr int XBATCH = 4;
+  constexpr int RED_QUADS = (WK - 1) * NT * 64;  // one parity half of the reduction area
+  static_assert(WK == 1 || WN == 1, "split tiles need every wave at every barrier");
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wk = wave % WK;
+  const int wn = wave / WK;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+
+  const int S = p.S;
+  const int T = p.T;
+  const int K = p.K;
+  const int N = p.N;
+  const int G = gridDim.x / S;
+  const int gi = blockIdx.x / S;
+  const int rank = blockIdx.x - gi * S;
+  const int kbase = rank * p.ks;
+  const int n_tiles = N / 16;
+  const int col = gi * WN + wn;   // this wave column's first tile
+  const int cstride = G * WN;     // distance between its tiles
+  const int ntl = (col < n_tiles) ? (n_tiles - col + cstride - 1) / cstride : 0;
+  const int cs = p.ks / STEP_K;             // load steps per tile (whole slice)
+  const int n_i = (cs - wk + WK - 1) / WK;  // this wave's steps per tile: j = wk + WK * i
+  const int total = ntl * n_i;
+
+  const uint32_t wrow_bytes = MX ? (uint32_t)(K / 2) : (uint32_t)K * 2u;
+  const rsrc_t wr = make_rsrc(p.w, (uint32_t)N * wrow_bytes);
+  const rsrc_t sr = MX ? make_rsrc(p.wscale, (uint32_t)N * (uint32_t)(K / 32)) : wr;
+  const rsrc_t xr = make_rsrc(p.x, (uint32_t)T * (uint32_t)K * 2u);
+
+  // X slot of (load step j, sub-step s, lane K block gg, token t): compact tile.
+  auto x_slot = [&](int j, int s, int gg, int t) -> int { return ((j * SUBS + s) * 4 + gg) * T + t; };
+  uint8_t* red_base = smem + (size_t)T * p.ks * 2;  // after the X slice, 16-byte aligned
+
+  // ---- prefetch position of this wave (wave-uniform) ---------------------
+  int pf_i = 0;
+  uint32_t pf_row = (uint32_t)(col * 16 + li) * wrow_bytes;  // byte offset of the lane's row
+  uint32_t pf_srow = (uint32_t)(col * 16 + li) * (uint32_t)(K / 32);
+  const uint32_t row_step = (uint32_t)(cstride * 16) * wrow_bytes;
+  const uint32_t srow_step = (uint32_t)(cstride * 16) * (uint32_t)(K / 32);
+  u32x4 ring[D][LOADS];
+  uint32_t sring[D];
+  int issued = 0;
+  auto issue = [&](int slot) {
+    const bool ok = issued < total;
+    const int kel = kbase + (wk + WK * pf_i) * STEP_K;
+    const uint32_t lo = MX ? (uint32_t)(kel / 2 + 16 * g) : (uint32_t)(kel * 2 + 16 * C * g);
+#pragma unroll
+    for (int l = 0; l < LOADS; ++l) ring[slot][l] = ld16_if(ok, wr, pf_row + lo + 16 * l);
+    if constexpr (MX) sring[slot] = ld1_if(ok, sr, pf_srow + (uint32_t)(kel / 32 + g));
+    ++issued;
+    if (++pf_i == n_i) {
+      pf_i = 0;
+      pf_row += row_step;
+      pf_srow += srow_step;
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < D; ++s) issue(s);
+
+  // ---- stage this rank's X slice once ------------------------------------
+  {
+    const int pieces = T * (p.ks / 8);
+    for (int p0 = tid; p0 < pieces; p0 += THREADS * XBATCH) {
+      u32x4 v[XBATCH];
+#pragma unroll
+      for (int b = 0; b < XBATCH; ++b) {
+        const int pc = p0 + b * THREADS;
+        const int t = pc % T;
+        const int k = (pc / T) * 8;
+        v[b] = ld16_if(pc < pieces, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(kbase + k)) * 2u);
+      }
+#pragma unroll
+      for (int b = 0; b < XBATCH; ++b) {
+        const int pc = p0 + b * THREADS;
+        if (pc < pieces) {
+          const int t = pc % T;
+          const int k = (pc / T) * 8;
+          int j, s2, gg;
+          if constexpr (MX) {
+            j = k / 128; gg = (k % 128) / 32; s2 = (k % 32) / 8;
+          } else {
+            j = k / (32 * C); gg = (k % (32 * C)) / (8 * C); s2 = (k % (8 * C)) / 8;
+          }
+          lds_write16(smem, x_slot(j, s2, gg, t), v[b]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc[NT];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const u32x4 (&a)[LOADS], uint32_t sc, int i) {
+    const int j = wk + WK * i;
+#pragma unroll
+    for (int s2 = 0; s2 < SUBS; ++s2) {
+      bf16x8 b[NT];
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        const int t = tt * 16 + li;
+        const bool ok = t < T;
+        const u32x4 v = lds_read16(smem, x_slot(j, s2, g, ok ? t : 0));
+        b[tt] = as_bf16x8(ok ? v : u32x4{0u, 0u, 0u, 0u});
+      }
+      bf16x8 af;
+      if constexpr (MX) {
+        af = fp4x8_bf16(a[0][s2], e8m0_f32(sc));
+      } else {
+        af = as_bf16x8(a[s2]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma_bf16(af, b[tt], acc[tt]);
+    }
+  };
+
+  const rsrc_t cr = make_rsrc(p.c, (uint32_t)T * (uint32_t)N * 2u);
+  const rsrc_t pr = make_rsrc(p.part, (uint32_t)S * (uint32_t)T * (uint32_t)N * 4u);
+
+  // End of one tile: wave-order sum through LDS (WK > 1), then the column's
+  // wave 0 stores.
+  auto tile_end = [&](int k) {
+    const int tile = col + cstride * k;
+    if constexpr (WK > 1) {
+      f32x4* red = reinterpret_cast<f32x4*>(red_base) + (k & 1) * RED_QUADS;
+      if (wk > 0) {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) red[((wk - 1) * NT + tt) * 64 + lane] = acc[tt];
+      }
+      __syncthreads();
+      if (wk == 0) {
+#pragma unroll 1
+        for (int w = 1; w < WK; ++w)
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) acc[tt] += red[((w - 1) * NT + tt) * 64 + lane];
+      }
+    }
+    if (wk == 0) {
+      const uint32_t n = (uint32_t)(tile * 16 + 4 * g);
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) {
+        const uint32_t t = (uint32_t)(tt * 16 + li);
+        const bool ok = (int)t < T;
+        if (S == 1) {
+          st8_if(ok, bf16_quad(acc[tt]), cr, (t * (uint32_t)N + n) * 2u);
+        } else {
+          st16_coherent_if(ok, __builtin_bit_cast(u32x4, acc[tt]), pr,
+                           (((uint32_t)rank * (uint32_t)T + t) * (uint32_t)N + n) * 4u);
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  int c_k = 0, c_i = 0;  // consume position
+  auto consumed = [&]() {
+    if (++c_i == n_i) {
+      tile_end(c_k);
+      c_i = 0;
+      ++c_k;
+    }
+  };
+
+  int q = 0;
+  for (; q + D <= total; q += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      compute(ring[s], sring[s], c_i);
+      issue(s);
+      __builtin_amdgcn_sched_barrier(0);
+      consumed();
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < D; ++s) {
+    if (q + s < total) {
+      compute(ring[s], sring[s], c_i);
+      consumed();
+    }
+  }
+  // A wave with no steps (slice shorter than WK steps) still takes part in
+  // every tile's reduction barrier.
+  if (n_i == 0) {
+    for (int k = 0; k < ntl; ++k) tile_end(k);
+  }
+
+  if (S == 1) return;
+
+  // ---- deferred split-K hand-off -----------------------------------------
+  wait_vmem_all();  // this wave's partial stores are complete (coherent)
+  int k0 = 0, kstep = 1;
+  if constexpr (WK > 1) {
+    __syncthreads();  // column wave 0's stores, seen by every wave of the column
+    k0 = wk;
+    kstep = WK;
+  }
+  for (int k = k0; k < ntl; k += kstep) {
+    const int tile = col + cstride * k;
+    uint32_t old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != (uint32_t)(S - 1)) continue;
+    if (lane == 0) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Last rank on this tile: partials of ranks 0..S-1 summed in rank order.
+    const uint32_t n = (uint32_t)(tile * 16 + 4 * g);
+#pragma unroll 1
+    for (int tt = 0; tt < NT; ++tt) {
+      const uint32_t t = (uint32_t)(tt * 16 + li);
+      const bool ok = (int)t < T;
+      f32x4 v[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (r < S)
+          v[r] = __builtin_bit_cast(
+              f32x4, ld16_coherent_if(ok, pr, (((uint32_t)r * (uint32_t)T + t) * (uint32_t)N + n) * 4u));
+      f32x4 tot = v[0];
+#pragma unroll
+      for (int r = 1; r < 8; ++r)
+        if (r < S) tot += v[r];
+      st8_if(ok, bf16_quad(tot), cr, (t * (uint32_t)N + n) * 2u);
     }
   }
 }
@@ -322,27 +587,35 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
 namespace {
 
 struct Shape {
-  int rg, wk, wn, d;
+  int rg, wk, wn, d, c;
+  int max_nt;  // largest token-tile count this shape is built for
 };
 
-// The instantiated workgroup shapes (per NT and weight format).
+// The instantiated workgroup shapes (each for NT = 1..8 and both weight
+// formats; MXFP4 ignores c: one 16-byte load is a whole scale block).
 constexpr Shape kShapes[] = {
-    {1, 4, 1, 8},  // tile_n 16: many small tiles for small N * split_k
-    {2, 4, 1, 8},  // tile_n 32
-    {4, 4, 1, 4},  // tile_n 64
-    {2, 2, 2, 4},  // tile_n 64, two waves share each staged X chunk
+    {1, 4, 1, 8, 2, 4},  // 0: 16 rows, 4 waves along K, 2 pieces per lane per step
+    {1, 8, 1, 8, 2, 4},  // 1: 16 rows, 8 waves along K
+    {1, 8, 1, 8, 1, 4},  // 2: 16 rows, 8 waves along K, 1 piece per step
+    {2, 2, 2, 4, 1, 8},  // 3: 64 rows, two wave columns share the staged X (large T)
+    {1, 4, 2, 8, 2, 4},  // 4: 32 rows, two wave columns share the staged X
+    {1, 2, 1, 4, 1, 8},  // 5: 16 rows, any T: the fallback when no larger tile divides N
 };
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 
-constexpr int kMaxXLds = 56 * 1024;  // LDS for the staged X chunk
-constexpr int kMaxLds = 60 * 1024;   // dynamic LDS per workgroup
+constexpr int kMaxXLds = 128 * 1024;  // LDS for the staged X slice (or chunk)
+constexpr int kMaxLds = 159 * 1024;   // dynamic LDS per workgroup (160 KiB per CU on gfx950)
 
 template <int NT, int SH, bool MX>
 hipError_t launch_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
   constexpr Shape sh = kShapes[SH];
-  auto kern = splitk_gemm_kernel<NT, sh.rg, sh.wk, sh.wn, sh.d, MX>;
-  hipLaunchKernelGGL(kern, dim3(t.grid), dim3(t.threads), t.lds, s, p);
-  return hipGetLastError();
+  if constexpr (NT > sh.max_nt) {
+    return hipErrorInvalidValue;  // not built: pick_tactic never selects it
+  } else {
+    auto kern = splitk_gemm_kernel<NT, sh.rg, sh.wk, sh.wn, sh.d, sh.c, MX>;
+    hipLaunchKernelGGL(kern, dim3(t.grid), dim3(t.threads), t.lds, s, p);
+    return hipGetLastError();
+  }
 }
 
 template <int NT, bool MX>
@@ -352,6 +625,8 @@ hipError_t launch_nt(int sh, const Tactic& t, const GemmParams& p, hipStream_t s
     case 1: return launch_one<NT, 1, MX>(t, p, s);
     case 2: return launch_one<NT, 2, MX>(t, p, s);
     case 3: return launch_one<NT, 3, MX>(t, p, s);
+    case 4: return launch_one<NT, 4, MX>(t, p, s);
+    case 5: return launch_one<NT, 5, MX>(t, p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -374,25 +649,145 @@ hipError_t launch_fmt(int sh, const Tactic& t, const GemmParams& p, hipStream_t 
 int shape_index(const Tactic& t) {
   for (int i = 0; i < kNumShapes; ++i)
     if (kShapes[i].rg == t.rg && kShapes[i].wk == t.wk && kShapes[i].wn == t.wn &&
-        kShapes[i].d == t.d)
+        kShapes[i].d == t.d && kShapes[i].c == t.c)
       return i;
   return -1;
 }
 
 // Largest chunk kc that divides ks, is a multiple of `step` and whose staged
-// X tile (tpad rows of bf16) fits in the LDS budget.
-int pick_kc(int ks, int step, int tpad) {
+// X tile (T rows of bf16) fits in the LDS budget. ks == 0 gives 0 (no chunk).
+int pick_kc(int ks, int step, int T) {
   if (ks == 0) return 0;
+  if (ks % step) return -1;
   const int units = ks / step;
   for (int m = 1; m <= units; ++m) {
     if (units % m) continue;
     const int kc = ks / m;
-    if ((long)tpad * kc * 2 <= kMaxXLds) return kc;
+    if ((long)T * kc * 2 <= kMaxXLds) return kc;
   }
   return -1;
 }
 
+// Fills the launch geometry of shape `si`; false if it does not fit.
+bool shape_fits(int si, int T, int N, int ks, int S, bool mx, Tactic* t) {
+  const Shape& c = kShapes[si];
+  if (t->nt > c.max_nt) return false;
+  const int tile_n = 16 * c.rg * c.wn;
+  if (N % tile_n) return false;
+  const int step = mx ? 128 : 32 * c.c;
+  const int kc = pick_kc(ks, step, T);
+  if (kc < 0) return false;
+  const int x_lds = T * kc * 2;
+  const int red_lds = (c.wk - 1) * c.wn * c.rg * t->nt * 64 * 16;
+  const int lds = x_lds > red_lds ? x_lds : red_lds;
+  if (lds > kMaxLds) return false;
+  t->rg = c.rg;
+  t->wk = c.wk;
+  t->wn = c.wn;
+  t->d = c.d;
+  t->c = c.c;
+  t->tile_n = tile_n;
+  t->threads = 64 * c.wk * c.wn;
+  t->kc = kc;
+  t->lds = lds;
+  t->grid = (N / tile_n) * S;
+  t->kind = 0;
+  t->shape = si;
+  return true;
+}
+
 }  // namespace
+
+// ---- persistent stream kernel configurations --------------------------
+
+struct StreamShape {
+  int wk, wn, d, c;
+};
+constexpr StreamShape kStreamShapes[] = {
+    {1, 8, 8, 2},  // 0: 8 waves, each streaming its own tiles
+    {1, 8, 8, 1},  // 1
+    {1, 4, 8, 2},  // 2
+    {8, 1, 8, 2},  // 3: 8 waves share each tile's K slice (LDS wave-order sum)
+    {8, 1, 8, 1},  // 4
+    {4, 1, 8, 1},  // 5
+};
+constexpr int kNumStreamShapes = sizeof(kStreamShapes) / sizeof(kStreamShapes[0]);
+constexpr int kStreamMaxNT = 2;
+constexpr int kStreamMaxX = 128 * 1024;
+
+template <int NT, int SH, bool MX>
+hipError_t launch_stream_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
+  constexpr StreamShape sh = kStreamShapes[SH];
+  auto kern = splitk_stream_kernel<NT, sh.wk, sh.wn, sh.d, sh.c, MX>;
+  hipLaunchKernelGGL(kern, dim3(t.grid), dim3(t.threads), t.lds, s, p);
+  return hipGetLastError();
+}
+
+template <int NT, bool MX>
+hipError_t launch_stream_nt(int sh, const Tactic& t, const GemmParams& p, hipStream_t s) {
+  switch (sh) {
+    case 0: return launch_stream_one<NT, 0, MX>(t, p, s);
+    case 1: return launch_stream_one<NT, 1, MX>(t, p, s);
+    case 2: return launch_stream_one<NT, 2, MX>(t, p, s);
+    case 3: return launch_stream_one<NT, 3, MX>(t, p, s);
+    case 4: return launch_stream_one<NT, 4, MX>(t, p, s);
+    case 5: return launch_stream_one<NT, 5, MX>(t, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool MX>
+hipError_t launch_stream_fmt(int sh, const Tactic& t, const GemmParams& p, hipStream_t s) {
+  switch (t.nt) {
+    case 1: return launch_stream_nt<1, MX>(sh, t, p, s);
+    case 2: return launch_stream_nt<2, MX>(sh, t, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* e = getenv(name);
+  return e ? atoi(e) : dflt;
+}
+
+// Fills the geometry of persistent shape `si`; false if it does not apply.
+bool stream_fits(int si, int T, int N, int ks, int S, bool mx, Tactic* t) {
+  const StreamShape& c = kStreamShapes[si];
+  if (t->nt > kStreamMaxNT || ks == 0) return false;
+  const int step = mx ? 128 : 32 * c.c;
+  if (ks % step) return false;
+  const int cs = ks / step;
+  if (cs < c.wk) return false;  // every wave needs at least one step per tile
+  const long x_lds = (long)T * ks * 2;
+  if (x_lds > kStreamMaxX) return false;
+  const int red = c.wk > 1 ? 2 * (c.wk - 1) * t->nt * 64 * 16 : 0;
+  const long lds = x_lds + red;
+  if (lds > kMaxLds) return false;
+  const int n_tiles = N / 16;
+  // Resident workgroups per CU: LDS-bound, at most 32 waves per CU.
+  const int waves = c.wk * c.wn;
+  int per_cu = (int)((160L * 1024) / (lds > 0 ? lds : 1));
+  if (per_cu > 32 / waves) per_cu = 32 / waves;
+  per_cu = env_int("SKGEMM_WG_PER_CU", per_cu < 2 ? per_cu : 2);
+  if (per_cu < 1) per_cu = 1;
+  long g = (256L * per_cu) / S;
+  const long g_max = (n_tiles + c.wn - 1) / c.wn;  // every column gets a tile
+  if (g > g_max) g = g_max;
+  if (g < 1) g = 1;
+  t->kind = 1;
+  t->rg = 1;
+  t->wk = c.wk;
+  t->wn = c.wn;
+  t->d = c.d;
+  t->c = c.c;
+  t->tile_n = 16;
+  t->threads = 64 * waves;
+  t->kc = ks;
+  t->lds = (int)lds;
+  t->grid = (int)g * S;
+  t->shape = si;
+  return true;
+}
 
 bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
   Tactic t{};
@@ -400,55 +795,56 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
   if (t.nt < 1) t.nt = 1;
   if (t.nt > 8) return false;
   t.mx = mx ? 1 : 0;
-  const int step = mx ? 128 : 32;
   const int ks = K / S;
+  const int tr = T > 0 ? T : 1;
 
-  // Shape choice: in order of preference (larger tiles re-read X less), the
-  // first whose tile divides N and that gives at least two workgroups per CU
-  // (256 CUs); failing that, the one giving the most workgroups.
-  static const int order_small_t[] = {2, 1, 0};
-  static const int order_large_t[] = {3, 2, 1, 0};
-  const int* order = (t.nt >= 4) ? order_large_t : order_small_t;
-  const int norder = (t.nt >= 4) ? 4 : 3;
-  int chosen = -1;
-  long best_wgs = -1;
-  int chosen_kc = -1, chosen_lds = 0;
-  const int tpad = 16 * t.nt;
-  for (int oi = 0; oi < norder; ++oi) {
-    const Shape& c = kShapes[order[oi]];
-    const int tile_n = 16 * c.rg * c.wn;
-    if (N % tile_n) continue;
-    const int kc = pick_kc(ks, step, tpad);
-    if (kc < 0) continue;
-    const int x_lds = tpad * kc * 2;
-    const int red_lds = (c.wk - 1) * c.wn * c.rg * t.nt * 64 * 16;
-    const int lds = x_lds > red_lds ? x_lds : red_lds;
-    if (lds > kMaxLds) continue;
-    const long wgs = (long)(N / tile_n) * S;
-    if (wgs >= 512 || wgs > best_wgs) {
-      best_wgs = wgs;
-      chosen = order[oi];
-      chosen_kc = kc;
-      chosen_lds = lds;
+  // Persistent streaming kernel first (SKGEMM_STREAM=-1 disables it,
+  // SKGEMM_STREAM=<index> forces one of its shapes, for tuning runs).
+  {
+    const int forced = env_int("SKGEMM_STREAM", -2);
+    if (forced >= 0 && forced < kNumStreamShapes && stream_fits(forced, tr, N, ks, S, mx, &t)) {
+      *out = t;
+      return true;
     }
-    if (wgs >= 512) break;
+    if (forced == -2) {
+      // Eight waves share each tile's K slice (measured fastest on the decode
+      // shapes: 16 weight rows open per workgroup, 8 streams on them); the
+      // one-wave-per-tile shapes remain for when the slice is too short.
+      static const int pref[] = {3, 4, 5, 0, 1, 2};
+      for (int si : pref) {
+        if (stream_fits(si, tr, N, ks, S, mx, &t)) {
+          *out = t;
+          return true;
+        }
+      }
+    }
   }
-  if (chosen < 0) return false;
-  const Shape& sh = kShapes[chosen];
-  t.rg = sh.rg;
-  t.wk = sh.wk;
-  t.wn = sh.wn;
-  t.d = sh.d;
-  t.tile_n = 16 * sh.rg * sh.wn;
-  t.threads = 64 * sh.wk * sh.wn;
-  t.kc = chosen_kc;
-  t.lds = chosen_lds;
-  t.grid = (N / t.tile_n) * S;
-  *out = t;
-  return true;
+  // A tiled shape forced for tuning runs (SKGEMM_SHAPE=<index>), if it fits.
+  if (const char* e = getenv("SKGEMM_SHAPE")) {
+    const int si = atoi(e);
+    if (si >= 0 && si < kNumShapes && shape_fits(si, tr, N, ks, S, mx, &t)) {
+      *out = t;
+      return true;
+    }
+  }
+  // Preference order: up to 32 tokens, 16-row tiles with 8 waves on each
+  // (few DRAM pages open per workgroup, deep prefetch); beyond, 64-row tiles
+  // whose two wave columns share the staged activations.
+  static const int small_t[] = {1, 2, 0, 4, 3, 5};
+  static const int large_t[] = {3, 4, 1, 2, 0, 5};
+  const int* order = (t.nt <= 2) ? small_t : large_t;
+  for (int oi = 0; oi < kNumShapes; ++oi) {
+    if (shape_fits(order[oi], tr, N, ks, S, mx, &t)) {
+      *out = t;
+      return true;
+    }
+  }
+  return false;
 }
 
 hipError_t launch_gemm(const Tactic& t, const GemmParams& p, hipStream_t s) {
+  if (t.kind == 1) return t.mx ? launch_stream_fmt<true>(t.shape, t, p, s)
+                               : launch_stream_fmt<false>(t.shape, t, p, s);
   const int sh = shape_index(t);
   if (sh < 0) return hipErrorInvalidValue;
   return t.mx ? launch_fmt<true>(sh, t, p, s) : launch_fmt<false>(sh, t, p, s);

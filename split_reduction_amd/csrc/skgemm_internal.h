@@ -21,21 +21,25 @@ struct GemmParams {
 };
 
 // A kernel configuration. One workgroup computes a TILE_N x T tile over one K
-// slice; its WK * WN waves split that slice WK ways along K (reduced through
-// LDS in wave order) and the tile WN ways along N; each wave owns RG groups
-// of 16 weight rows and keeps D load steps of weights in flight per group.
+// slice; its WK * WN waves split that slice WK ways along K (interleaved load
+// steps, reduced through LDS in wave order) and the tile WN ways along N;
+// each wave owns RG groups of 16 weight rows and keeps D load steps of
+// weights in flight per group.
 struct Tactic {
   int nt;       // 16-token MFMA tiles: T_pad = 16 * nt, 1..8
   int rg;       // 16-row groups per wave
   int wk;       // waves along K
   int wn;       // waves along N
   int d;        // weight load steps in flight per row group
+  int c;        // 16-byte weight pieces per lane per load step (bf16)
   int kc;       // K chunk staged in LDS
   int tile_n;   // 16 * rg * wn
   int threads;  // 64 * wk * wn
   int lds;      // dynamic LDS bytes
   int grid;     // workgroups = (N / tile_n) * split_k
   int mx;       // 1 for MXFP4 weights
+  int kind;     // 0: one tile per workgroup; 1: persistent stream kernel
+  int shape;    // index into the kind's shape table
 };
 
 // Picks the configuration for a launch over T <= 128 rows; returns false if no

@@ -91,16 +91,23 @@ def test_strerror_covers_every_code():
     (24, 16384, 16384, 4, False),
     (128, 16384, 16384, 2, False),
     (300, 256, 1024, 1, False),
+    (200, 96, 256, 2, False),
+    (130, 64, 256, 1, True),
 ])
 def test_tactics_cover_the_workloads(T, N, K, S, mx):
     _ensure_built()
     t = sk.skgemm_tactic_for(T, N, K, S, mx)
     assert t["nt"] == min((min(T, 128) + 15) // 16, 8)
     assert N % t["tile_n"] == 0
-    assert t["grid"] == (N // t["tile_n"]) * S
+    if t["kind"] == "tiled":
+        assert t["grid"] == (N // t["tile_n"]) * S
+    else:  # persistent: G workgroups per split rank, every wave column owns a tile
+        assert t["grid"] % S == 0 and t["tile_n"] == 16
+        assert 1 <= (t["grid"] // S - 1) * t["wn"] < N // 16
+        assert t["kc"] == K // S
     assert (K // S) % t["kc"] == 0
-    assert t["lds"] <= 64 * 1024
+    assert t["lds"] <= 159 * 1024
     assert t["token_blocks"] == (T + 127) // 128
     step = 128 if mx else 32
     assert t["kc"] % step == 0
-    assert 16 * t["nt"] * t["kc"] * 2 <= 64 * 1024
+    assert min(T, 128) * t["kc"] * 2 <= 128 * 1024

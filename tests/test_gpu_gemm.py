@@ -223,3 +223,54 @@ def test_bf16_sweep_sampled_parity(T, sweep_weights):
     ref = G.gemm_bf16_ref(x, wb[rows])
     # the rms of the sampled columns estimates the full output's rms
     assert_parity(c[:, rows], ref, w.K, f"sweep T={T} (1024 sampled features)")
+
+
+def test_graph_replays_match_eager():
+    """Captured into a HIP graph (workspace reserved first), every replay gives
+    the eager bits, with eager work and synchronisations between replays."""
+    t = torch()
+    w = workloads.WORKLOADS["bf16_t32_k7168_n18432"]
+    T, N, K, S = 32, 2048, 7168, 8
+    log("graph capture and replays, T=32 N=2048 K=7168 S=8")
+    x, wb = workloads.small_bf16_case(T, K, N, seed=71)
+    W, X = to_dev_bf16(wb), to_dev_bf16(x)
+    eager = run_bf16(x, None, S, W=W)
+    s = t.cuda.Stream()
+    sk.skgemm_reserve(T, N, S, s)
+    C = empty_bf16(T, N)
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g, stream=s):
+        sk.skgemm_bf16(W, X, C, T, N, K, S, s)
+    for rep in range(4):
+        C.zero_()
+        g.replay()
+        t.cuda.synchronize()
+        assert np.array_equal(bf16_bits(C), eager), f"replay {rep}"
+        # eager work on the default stream between replays
+        other = run_bf16(x[:5], None, 4, W=W)
+        assert other.shape == (5, N)
+    assert w.K == K
+
+
+# Every instantiated kernel shape, forced through the tuning variables the
+# tactic reads (SKGEMM_STREAM selects a persistent-kernel shape or -1 to turn
+# it off, SKGEMM_SHAPE a one-tile-per-workgroup shape), on shapes with ragged
+# T, uneven step counts per wave and several tiles per wave column.
+FORCED = [("SKGEMM_STREAM", str(i)) for i in range(6)] + [("SKGEMM_SHAPE", str(i)) for i in range(6)]
+
+
+@pytest.mark.parametrize("var,val", FORCED)
+def test_every_kernel_shape(var, val, monkeypatch):
+    if var == "SKGEMM_SHAPE":
+        monkeypatch.setenv("SKGEMM_STREAM", "-1")
+    monkeypatch.setenv(var, val)
+    for (T, N, K, S) in [(3, 512, 1792, 4), (24, 1024, 2048, 8), (17, 256, 7168, 2), (1, 4096, 512, 1)]:
+        tac = sk.skgemm_tactic_for(T, N, K, S)
+        log(f"forced {var}={val}: bf16 T={T} N={N} K={K} S={S} tactic={tac}")
+        x, w = workloads.small_bf16_case(T, K, N, seed=5000 + T + S)
+        assert_parity(run_bf16(x, w, S), G.gemm_bf16_ref(x, w), K, f"{var}={val} T={T} S={S}")
+    for (T, N, K, S) in [(5, 512, 2048, 4), (30, 256, 1024, 2)]:
+        tac = sk.skgemm_tactic_for(T, N, K, S, True)
+        log(f"forced {var}={val}: mxfp4 T={T} N={N} K={K} S={S} tactic={tac}")
+        x, wq, ws = workloads.small_mxfp4_case(T, K, N, seed=6000 + T + S)
+        assert_parity(run_mxfp4(x, wq, ws, S), G.gemm_mxfp4_ref(x, wq, ws), K, f"{var}={val} mx T={T}")
