@@ -21,7 +21,13 @@ T) are timed the same way and reported under "workloads". The cpu_baseline
 leg times the fp64 oracle on the host on the headline workload.
 
 ``--trace-summary DIR`` reads a rocprofv3 kernel trace written under DIR and
-prints per-workload kernel durations (matched by kernel name and grid size).
+prints per-workload kernel durations (runs of dispatches in time order).
+
+``--pmc-run`` is the short program the HBM counters are taken on: 10 eager
+headline launches on rotated weights, then 5 plain device copies of 256 MiB
+(which read and write exactly 256 MiB each) that calibrate the counters.
+``--pmc-summary DIR`` turns the rocprofv3 counter CSVs under DIR into bytes
+per launch.
 """
 
 from __future__ import annotations
@@ -256,6 +262,54 @@ def trace_summary(path: str, steps: int, warmup: int) -> None:
             print(f"headline cache-resident timed replay: {len(hot)} launches, avg {hot.mean():.3f} us")
 
 
+COPY_BYTES = 256 << 20
+
+
+def pmc_run() -> None:
+    import torch
+
+    import split_reduction_amd as sk
+
+    head = workloads.WORKLOADS[HEADLINE]
+    case = Case(head)
+    stream = torch.cuda.current_stream()
+    for i in range(10):
+        case.launch(i, stream)
+    torch.cuda.synchronize()
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0").random_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del sk
+    print(json.dumps({"pmc_run": HEADLINE, "launches": 10, "copies": 5, "copy_bytes": COPY_BYTES}))
+
+
+def pmc_summary(path: str) -> dict:
+    """Average counter value per dispatch for the GEMM kernel and the copy."""
+    import csv
+
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    vals = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r.get("Kernel_Name", "")
+                kind = "gemm" if "splitk_" in name else ("copy" if "copy" in name.lower() or "elementwise" in name.lower() else None)
+                if kind is None:
+                    continue
+                cname = r.get("Counter_Name", "")
+                vals.setdefault((kind, cname), []).append(float(r.get("Counter_Value", "nan")))
+    out = {}
+    for (kind, cname), v in sorted(vals.items()):
+        out[f"{kind}:{cname}"] = {"dispatches": len(v), "avg": float(np.mean(v))}
+        print(f"{kind:5s} {cname:12s} dispatches {len(v):4d}  avg {np.mean(v):14.1f}")
+    return out
+
+
 # ---------------------------------------------------------------------------
 
 
@@ -280,7 +334,15 @@ def main() -> None:
     ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-summary", metavar="DIR", help="summarise a rocprofv3 kernel trace and exit")
+    ap.add_argument("--pmc-run", action="store_true", help="the short run HBM counters are taken on")
+    ap.add_argument("--pmc-summary", metavar="DIR", help="summarise rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
+    if args.pmc_run:
+        pmc_run()
+        return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.steps, args.warmup)
         return
