@@ -263,6 +263,8 @@ def trace_summary(path: str, steps: int, warmup: int) -> None:
 
 
 COPY_BYTES = 256 << 20
+PMC_LAUNCHES = 10
+PMC_COPIES = 5
 
 
 def pmc_run() -> None:
@@ -273,40 +275,79 @@ def pmc_run() -> None:
     head = workloads.WORKLOADS[HEADLINE]
     case = Case(head)
     stream = torch.cuda.current_stream()
-    for i in range(10):
+    for i in range(PMC_LAUNCHES):
         case.launch(i, stream)
     torch.cuda.synchronize()
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0").random_()
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    for _ in range(5):
+    for _ in range(PMC_COPIES):
         dst.copy_(src)
     torch.cuda.synchronize()
     del sk
-    print(json.dumps({"pmc_run": HEADLINE, "launches": 10, "copies": 5, "copy_bytes": COPY_BYTES}))
+    print(json.dumps({"pmc_run": HEADLINE, "launches": PMC_LAUNCHES, "copies": PMC_COPIES,
+                      "copy_bytes": COPY_BYTES}))
 
 
 def pmc_summary(path: str) -> dict:
-    """Average counter value per dispatch for the GEMM kernel and the copy."""
+    """HBM bytes per headline launch from the FETCH_SIZE and WRITE_SIZE passes
+    of ``--pmc-run`` under ``path`` (KiB per dispatch, each scaled by what the
+    same counter reads for the 256 MiB calibration copies: the last
+    ``copies`` copyBuffer dispatches of the run)."""
     import csv
 
-    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no counter_collection.csv under {path}")
-    vals = {}
-    for f in files:
-        with open(f) as fh:
-            for r in csv.DictReader(fh):
-                name = r.get("Kernel_Name", "")
-                kind = "gemm" if "splitk_" in name else ("copy" if "copy" in name.lower() or "elementwise" in name.lower() else None)
-                if kind is None:
-                    continue
-                cname = r.get("Counter_Name", "")
-                vals.setdefault((kind, cname), []).append(float(r.get("Counter_Value", "nan")))
-    out = {}
-    for (kind, cname), v in sorted(vals.items()):
-        out[f"{kind}:{cname}"] = {"dispatches": len(v), "avg": float(np.mean(v))}
-        print(f"{kind:5s} {cname:12s} dispatches {len(v):4d}  avg {np.mean(v):14.1f}")
+    per = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = []
+        for f in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
+            with open(f) as fh:
+                rows += [r for r in csv.DictReader(fh) if r.get("Counter_Name") == counter]
+        if not rows:
+            raise SystemExit(f"no {counter} rows under {path}")
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        gemm = [float(r["Counter_Value"]) for r in rows if "splitk_" in r["Kernel_Name"]]
+        kernels = sorted({r["Kernel_Name"] for r in rows if "splitk_" in r["Kernel_Name"]})
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-PMC_COPIES:]
+        if len(gemm) != PMC_LAUNCHES or len(copies) != PMC_COPIES or len(kernels) != 1:
+            raise SystemExit(f"{counter}: {len(gemm)} GEMM dispatches of {kernels}, {len(copies)} copies")
+        per[counter] = (float(np.mean(gemm)), float(np.mean(copies)), kernels[0])
+    fetch, fetch_copy, kname = per["FETCH_SIZE"]
+    write, write_copy, _ = per["WRITE_SIZE"]
+    fetch_factor = fetch_copy * 1024 / COPY_BYTES
+    write_factor = write_copy * 1024 / COPY_BYTES
+    rd = fetch * 1024 / fetch_factor
+    wr = write * 1024 / write_factor
+    head = workloads.WORKLOADS[HEADLINE]
+    algo = head.weight_bytes() + head.T * head.K * 2 + head.T * head.N * 2
+    out = {
+        "workload": HEADLINE,
+        "kernel": kname.split("(")[0].replace("void ", ""),
+        "kernel_source_sha": kernel_source_hash(),
+        "fetch_size_kib_per_launch": round(fetch, 1),
+        "write_size_kib_per_launch": round(write, 1),
+        "copy_calibration": {
+            "bytes_read_and_written": COPY_BYTES,
+            "fetch_size_kib": round(fetch_copy, 1),
+            "write_size_kib": round(write_copy, 1),
+            "fetch_kib_x1024_per_byte": round(fetch_factor, 4),
+            "write_kib_x1024_per_byte": round(write_factor, 4),
+        },
+        "hbm_read_bytes_per_launch": int(round(rd)),
+        "hbm_write_bytes_per_launch": int(round(wr)),
+        "hbm_bytes_per_launch": int(round(rd + wr)),
+        "algorithmic_bytes_per_launch": algo,
+        "commands": [
+            "cd /tmp && timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE --output-format csv "
+            "-d $R/gpurun_out/pmc/fetch -o fetch -- python3 $R/bench.py --pmc-run",
+            "cd /tmp && timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE --output-format csv "
+            "-d $R/gpurun_out/pmc/write -o write -- python3 $R/bench.py --pmc-run",
+            "python bench.py --pmc-summary gpurun_out/pmc",
+        ],
+        "note": (f"R is the repository root. Counters are per dispatch: {PMC_LAUNCHES} headline "
+                 f"launches on rotated weights, then {PMC_COPIES} copies of {COPY_BYTES >> 20} MiB "
+                 "whose counter readings calibrate KiB per byte moved."),
+    }
+    print(json.dumps(out, indent=1))
     return out
 
 

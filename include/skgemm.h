@@ -154,6 +154,19 @@ SKGEMM_API int skgemm_wave_sum(const float* in, float* out, size_t n_waves, hipS
 SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int mxfp4, char* buf,
                                  size_t buf_len);
 
+/*
+ * skgemm_set_timeline: opt-in phase stamps of the persistent stream kernel
+ * (page vllm.models.deepseek_v41.amd.mono.common.ops, module note and
+ * memrealtime: timeline phase stamps from s_memrealtime, the 100 MHz device
+ * clock). While set, every workgroup w of a stream-kernel launch writes five
+ * uint64 clock values to buf[8*w .. 8*w+4]: kernel entry, X staged in LDS,
+ * weight stream done, own partial stores complete, exit. Device memory,
+ * caller-owned, 8-byte aligned; `capacity` is its length in uint64. Launches
+ * whose grid needs more than capacity/8 workgroups write nothing. Pass
+ * buf = NULL to turn stamping off (the default). Process-wide setting.
+ */
+SKGEMM_API int skgemm_set_timeline(void* buf, size_t capacity);
+
 /* skgemm_strerror: static text for a return code. */
 SKGEMM_API const char* skgemm_strerror(int code);
 

@@ -48,6 +48,7 @@ def _declare(lib):
         "skgemm_wave_sum": [vp, vp, sz, st],
         "skgemm_tactic_for": [i, i, i, i, i, ctypes.c_char_p, sz],
         "skgemm_last_hip_error": [],
+        "skgemm_set_timeline": [vp, sz],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -146,6 +147,11 @@ def skgemm_tactic_for(T: int, N: int, K: int, split_k: int, mxfp4: bool = False)
     code = lib().skgemm_tactic_for(T, N, K, split_k, 1 if mxfp4 else 0, buf, len(buf))
     _check(code, "skgemm_tactic_for")
     return json.loads(buf.value.decode())
+
+
+def skgemm_set_timeline(buf, capacity: int) -> None:
+    """Opt-in per-workgroup phase stamps of the stream kernel (None turns them off)."""
+    _check(lib().skgemm_set_timeline(_ptr(buf), capacity if buf is not None else 0), "skgemm_set_timeline")
 
 
 def skgemm_strerror(code: int) -> str:

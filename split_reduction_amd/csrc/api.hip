@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -17,6 +18,10 @@ namespace {
 constexpr int kTokenBlock = 128;  // rows of X / C per launch (16 * 8 MFMA tiles)
 
 thread_local int g_last_hip_error = 0;
+
+// Optional phase-stamp buffer (skgemm_set_timeline).
+std::atomic<uint64_t*> g_stamps{nullptr};
+std::atomic<size_t> g_stamps_cap{0};
 
 int hip_fail(hipError_t e) {
   g_last_hip_error = (int)e;
@@ -132,6 +137,7 @@ int run_gemm(bool mx, const void* w, const void* ws, const void* x, void* c, int
     p.ks = K / S;
     p.kc = tac.kc;
     p.nchunks = (tac.kc > 0) ? p.ks / tac.kc : 0;
+    p.stamps = ((size_t)tac.grid * 8 <= g_stamps_cap.load()) ? g_stamps.load() : nullptr;
     hipError_t e = skg::launch_gemm(tac, p, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -222,10 +228,17 @@ SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int mxfp4, ch
     snprintf(buf, buf_len,
              "{\"nt\": %d, \"rg\": %d, \"wk\": %d, \"wn\": %d, \"d\": %d, \"c\": %d, \"kc\": %d, "
              "\"tile_n\": %d, \"threads\": %d, \"lds\": %d, \"grid\": %d, \"split_k\": %d, "
-             "\"token_blocks\": %d, \"mxfp4\": %d, \"kind\": \"%s\"}",
+             "\"token_blocks\": %d, \"mxfp4\": %d, \"kind\": \"%s\", \"shape\": %d}",
              t.nt, t.rg, t.wk, t.wn, t.d, t.c, t.kc, t.tile_n, t.threads, t.lds, t.grid, split_k,
-             blocks, t.mx, t.kind == 1 ? "stream" : "tiled");
+             blocks, t.mx, t.kind == 1 ? "stream" : "tiled", t.shape);
   }
+  return SKGEMM_OK;
+}
+
+SKGEMM_API int skgemm_set_timeline(void* buf, size_t capacity) {
+  if (buf != nullptr && ((uintptr_t)buf & 7u) != 0) return SKGEMM_EALIGN;
+  g_stamps_cap.store(buf ? capacity : 0);
+  g_stamps.store(static_cast<uint64_t*>(buf));
   return SKGEMM_OK;
 }
 

@@ -47,6 +47,15 @@ namespace skg {
 
 namespace {
 
+// Workgroups of the stream kernel the grid sizing assumes resident per CU:
+// two when one token tile suffices, one otherwise (the X slice of up to 32
+// tokens then fills most of the LDS anyway). The kernel's register budget is
+// pinned to match (waves per SIMD = resident waves / 4).
+constexpr int stream_wgs_per_cu(int nt) { return nt == 1 ? 2 : 1; }
+constexpr int stream_waves_per_eu(int nt, int waves) {
+  return (stream_wgs_per_cu(nt) * waves + 3) / 4 > 0 ? (stream_wgs_per_cu(nt) * waves + 3) / 4 : 1;
+}
+
 __device__ __forceinline__ u32x4 lds_read16(const uint8_t* smem, int slot) {
   return *reinterpret_cast<const u32x4*>(smem + slot * 16);
 }
@@ -324,34 +333,51 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
 // Persistent streaming kernel (16-row tiles, X staged once per workgroup)
 // ---------------------------------------------------------------------------
 //
-// grid = S * G workgroups of WK * WN waves; workgroup (gi, rank) owns K slice
-// `rank`. Its WN wave columns each own a list of 16-row tiles (column
-// gi*WN + wn takes tiles gi*WN + wn, + G*WN, ...); the WK waves of a column
-// split every tile's K slice (interleaved load steps). The workgroup stages
-// its X slice in LDS once, shared by all its waves; each wave then streams
-// the weight rows of all its tiles through one D-deep register ring that runs
-// on across tile boundaries, so neither the staging nor the load latency is
-// paid per tile. At a tile's end the WK waves' partial sums meet in LDS
-// (wave order, WK > 1 only) and the column's wave 0 writes the tile's FP32
-// partial (device-coherent) or, without a split, the bf16 output. The
-// hand-off is deferred to the end: one wait for all stores, then one counter
-// atomic per tile; the last rank to arrive on a tile sums the ranks'
-// partials in rank order and stores C. Waiting for stores mid-stream would
-// drain the ring (loads and stores share one counter and may complete out
-// of order relative to each other), which is why nothing is signalled early.
-// With WK > 1 the host uses WN = 1, so every wave meets the same barriers.
-template <int NT, int WK, int WN, int D, int C, bool MX>
-__global__ __launch_bounds__(64 * WK * WN) void splitk_stream_kernel(GemmParams p) {
+// grid = S * G workgroups; workgroup (gi, rank) owns K slice `rank` and stages
+// that slice of X in LDS once, shared by all its waves for all its tiles.
+// Weights stream through one D-deep register ring per wave that runs on
+// across tile boundaries, so neither the staging nor the load latency is
+// paid per tile. Three organisations of the waves:
+//
+// * WK > 1, EPI = 0: all WK waves stream, splitting every tile's K slice
+//   (interleaved load steps). At a tile's end they meet in LDS; wave 0 adds
+//   the others' sums in wave order (the pages' row_sum) and stores the tile's
+//   FP32 partial (device-coherent) or, without a split, the bf16 output.
+// * WK > 1, EPI = 1: wave 0 is a dedicated epilogue wave (the pages'
+//   SplitKGemm keeps weight, MMA and epilogue roles in separate warps) and
+//   waves 1..WK-1 stream. The epilogue wave sums the parked partials in wave
+//   order and runs the split-K hand-off as a per-tile pipeline: store the
+//   partial, one tile later bump the tile's counter, one tile later load the
+//   ranks' partials if it arrived last, one tile later sum them in rank order
+//   and store C, waiting only for its own operations of the previous stage.
+// * WK == 1: each of the WN waves streams its own tiles (column gi*WN + wn
+//   takes tiles gi*WN + wn, + G*WN, ...) and stores its own partials.
+//
+// Without an epilogue wave the hand-off is deferred to the workgroup's end:
+// loads and stores share one completion counter and may complete out of order
+// relative to each other, so waiting for a store mid-stream would drain the
+// ring. At the end each wave takes every WK-th tile: one vector atomic bumps
+// all their counters (a lane per tile) and the tiles it arrived last on are
+// finished two at a time, all partial loads in flight before the sums.
+template <int NT, int WK, int WN, int D, int C, bool EPI, bool MX>
+__global__ __launch_bounds__(64 * WK * WN)
+__attribute__((amdgpu_waves_per_eu(stream_waves_per_eu(NT, WK * WN))))
+void splitk_stream_kernel(GemmParams p) {
   constexpr int THREADS = 64 * WK * WN;
   constexpr int LOADS = MX ? 1 : C;
   constexpr int SUBS = MX ? 4 : C;
   constexpr int STEP_K = MX ? 128 : 32 * C;
   constexpr int XBATCH = 4;
-  constexpr int RED_QUADS = (WK - 1) * NT * 64;  // one parity half of the reduction area
-  static_assert(WK == 1 || WN == 1, "split tiles need every wave at every barrier");
+  constexpr int SWK = EPI ? WK - 1 : WK;   // streaming waves per tile
+  constexpr int PARKED = EPI ? SWK : WK - 1;  // partial sums parked in LDS per tile
+  constexpr int RED_QUADS = (PARKED > 0 ? PARKED : 1) * NT * 64;  // one parity half
+  static_assert(WK == 1 || WN == 1, "waves that split a tile form one column");
+  static_assert(!EPI || WK > 1, "an epilogue wave needs streaming waves");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
+  uint64_t stamp[5];  // optional phase stamps (s_memrealtime, 100 MHz)
+  stamp[0] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -359,6 +385,8 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_stream_kernel(GemmParams 
   const int wn = wave / WK;
   const int g = lane >> 4;
   const int li = lane & 15;
+  const bool epi_wave = EPI && wave == 0;
+  const int sw = EPI ? wk - 1 : wk;  // index among the streaming waves of the tile
 
   const int S = p.S;
   const int T = p.T;
@@ -372,22 +400,24 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_stream_kernel(GemmParams 
   const int col = gi * WN + wn;   // this wave column's first tile
   const int cstride = G * WN;     // distance between its tiles
   const int ntl = (col < n_tiles) ? (n_tiles - col + cstride - 1) / cstride : 0;
-  const int cs = p.ks / STEP_K;             // load steps per tile (whole slice)
-  const int n_i = (cs - wk + WK - 1) / WK;  // this wave's steps per tile: j = wk + WK * i
+  const int cs = p.ks / STEP_K;  // load steps per tile (whole slice)
+  const int n_i = epi_wave ? 0 : (cs - sw + SWK - 1) / SWK;  // this wave's steps per tile
   const int total = ntl * n_i;
 
   const uint32_t wrow_bytes = MX ? (uint32_t)(K / 2) : (uint32_t)K * 2u;
   const rsrc_t wr = make_rsrc(p.w, (uint32_t)N * wrow_bytes);
   const rsrc_t sr = MX ? make_rsrc(p.wscale, (uint32_t)N * (uint32_t)(K / 32)) : wr;
   const rsrc_t xr = make_rsrc(p.x, (uint32_t)T * (uint32_t)K * 2u);
+  const rsrc_t cr = make_rsrc(p.c, (uint32_t)T * (uint32_t)N * 2u);
+  const rsrc_t pr = make_rsrc(p.part, (uint32_t)S * (uint32_t)T * (uint32_t)N * 4u);
 
   // X slot of (load step j, sub-step s, lane K block gg, token t): compact tile.
   auto x_slot = [&](int j, int s, int gg, int t) -> int { return ((j * SUBS + s) * 4 + gg) * T + t; };
-  uint8_t* red_base = smem + (size_t)T * p.ks * 2;  // after the X slice, 16-byte aligned
+  f32x4* red_base = reinterpret_cast<f32x4*>(smem + (size_t)T * p.ks * 2);  // 16-byte aligned
 
-  // ---- prefetch position of this wave (wave-uniform) ---------------------
+  // ---- weight ring (streaming waves) -------------------------------------
   int pf_i = 0;
-  uint32_t pf_row = (uint32_t)(col * 16 + li) * wrow_bytes;  // byte offset of the lane's row
+  uint32_t pf_row = (uint32_t)(col * 16 + li) * wrow_bytes;
   uint32_t pf_srow = (uint32_t)(col * 16 + li) * (uint32_t)(K / 32);
   const uint32_t row_step = (uint32_t)(cstride * 16) * wrow_bytes;
   const uint32_t srow_step = (uint32_t)(cstride * 16) * (uint32_t)(K / 32);
@@ -396,7 +426,7 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_stream_kernel(GemmParams 
   int issued = 0;
   auto issue = [&](int slot) {
     const bool ok = issued < total;
-    const int kel = kbase + (wk + WK * pf_i) * STEP_K;
+    const int kel = kbase + (sw + SWK * pf_i) * STEP_K;
     const uint32_t lo = MX ? (uint32_t)(kel / 2 + 16 * g) : (uint32_t)(kel * 2 + 16 * C * g);
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) ring[slot][l] = ld16_if(ok, wr, pf_row + lo + 16 * l);
@@ -409,46 +439,155 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_stream_kernel(GemmParams 
     }
   };
 
-#pragma unroll
-  for (int s = 0; s < D; ++s) issue(s);
-
   // ---- stage this rank's X slice once ------------------------------------
-  {
-    const int pieces = T * (p.ks / 8);
-    for (int p0 = tid; p0 < pieces; p0 += THREADS * XBATCH) {
-      u32x4 v[XBATCH];
+  // The first batch of X loads goes out before the weight prologue, so its
+  // LDS writes wait only for X (loads complete in issue order) and the
+  // multiplies can start while the weights are still arriving.
+  const int pieces = T * (p.ks / 8);
+  auto stage_load = [&](int p0, u32x4 (&v)[XBATCH]) {
 #pragma unroll
-      for (int b = 0; b < XBATCH; ++b) {
-        const int pc = p0 + b * THREADS;
+    for (int b = 0; b < XBATCH; ++b) {
+      const int pc = p0 + b * THREADS;
+      const int t = pc % T;
+      const int k = (pc / T) * 8;
+      v[b] = ld16_if(pc < pieces, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(kbase + k)) * 2u);
+    }
+  };
+  auto stage_store = [&](int p0, const u32x4 (&v)[XBATCH]) {
+#pragma unroll
+    for (int b = 0; b < XBATCH; ++b) {
+      const int pc = p0 + b * THREADS;
+      if (pc < pieces) {
         const int t = pc % T;
         const int k = (pc / T) * 8;
-        v[b] = ld16_if(pc < pieces, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(kbase + k)) * 2u);
-      }
-#pragma unroll
-      for (int b = 0; b < XBATCH; ++b) {
-        const int pc = p0 + b * THREADS;
-        if (pc < pieces) {
-          const int t = pc % T;
-          const int k = (pc / T) * 8;
-          int j, s2, gg;
-          if constexpr (MX) {
-            j = k / 128; gg = (k % 128) / 32; s2 = (k % 32) / 8;
-          } else {
-            j = k / (32 * C); gg = (k % (32 * C)) / (8 * C); s2 = (k % (8 * C)) / 8;
-          }
-          lds_write16(smem, x_slot(j, s2, gg, t), v[b]);
+        int j, s2, gg;
+        if constexpr (MX) {
+          j = k / 128; gg = (k % 128) / 32; s2 = (k % 32) / 8;
+        } else {
+          j = k / (32 * C); gg = (k % (32 * C)) / (8 * C); s2 = (k % (8 * C)) / 8;
         }
+        lds_write16(smem, x_slot(j, s2, gg, t), v[b]);
       }
+    }
+  };
+  {
+    u32x4 v[XBATCH];
+    stage_load(tid, v);
+    if (!epi_wave) {
+#pragma unroll
+      for (int s = 0; s < D; ++s) issue(s);
+    }
+    stage_store(tid, v);
+    for (int p0 = tid + THREADS * XBATCH; p0 < pieces; p0 += THREADS * XBATCH) {
+      stage_load(p0, v);
+      stage_store(p0, v);
     }
   }
   __syncthreads();
+  stamp[1] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
 
+  // Thread 0 of each workgroup writes the stamps (vector stores).
+  auto write_stamps = [&]() {
+    if (p.stamps != nullptr && tid == 0) {
+      stamp[4] = __builtin_amdgcn_s_memrealtime();
+      const rsrc_t sr8 = make_rsrc(p.stamps + (size_t)blockIdx.x * 8, 64);
+#pragma unroll
+      for (int i = 0; i < 5; ++i)
+        st8_if(true, u32x2{(uint32_t)stamp[i], (uint32_t)(stamp[i] >> 32)}, sr8, 8u * i);
+    }
+  };
+
+  // C / partial offsets of this lane's quad (token tt*16 + li, features
+  // tile*16 + 4g .. +3).
+  auto c_off = [&](int tile, int tt) -> uint32_t {
+    return ((uint32_t)(tt * 16 + li) * (uint32_t)N + (uint32_t)(tile * 16 + 4 * g)) * 2u;
+  };
+  auto p_off = [&](int r, int tile, int tt) -> uint32_t {
+    return (((uint32_t)r * (uint32_t)T + (uint32_t)(tt * 16 + li)) * (uint32_t)N +
+            (uint32_t)(tile * 16 + 4 * g)) * 4u;
+  };
+  auto in_t = [&](int tt) -> bool { return tt * 16 + li < T; };
+
+  if constexpr (EPI) {
+    if (epi_wave) {
+      // ---- epilogue wave: wave-order sum and pipelined hand-off -----------
+      int st_tile = -1;  // partial stores issued last stage
+      int at_tile = -1;  // counter atomic issued last stage
+      uint32_t at_old = 0;
+      int ld_tile = -1;  // partial loads issued last stage
+      f32x4 ld[NT][8];
+      auto finish_stage = [&]() {
+        wait_vmem_all();  // everything issued at the previous stage has completed
+        if (ld_tile >= 0) {  // last arriver: rank-ordered sum, one bf16 store
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) {
+            f32x4 tot = ld[tt][0];
+#pragma unroll
+            for (int r = 1; r < 8; ++r)
+              if (r < S) tot += ld[tt][r];
+            st8_if(in_t(tt), bf16_quad(tot), cr, c_off(ld_tile, tt));
+          }
+          ld_tile = -1;
+        }
+        if (at_tile >= 0) {
+          const uint32_t old = __builtin_amdgcn_readfirstlane(at_old);
+          if (old == (uint32_t)(S - 1)) {
+            if (lane == 0)
+              __hip_atomic_store(p.cnt + at_tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+              for (int r = 0; r < 8; ++r)
+                if (r < S)
+                  ld[tt][r] = __builtin_bit_cast(f32x4, ld16_coherent_if(in_t(tt), pr, p_off(r, at_tile, tt)));
+            ld_tile = at_tile;
+          }
+          at_tile = -1;
+        }
+        if (st_tile >= 0) {  // its partial stores are complete: signal
+          if (lane == 0)
+            at_old = __hip_atomic_fetch_add(p.cnt + st_tile, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+          at_tile = st_tile;
+          st_tile = -1;
+        }
+      };
+      for (int k = 0; k < ntl; ++k) {
+        __syncthreads();  // tile k's partial sums are in LDS
+        const int tile = col + cstride * k;
+        const f32x4* red = red_base + (k & 1) * RED_QUADS;
+        f32x4 acc[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) acc[tt] = red[tt * 64 + lane];
+#pragma unroll 1
+        for (int w = 1; w < SWK; ++w)
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) acc[tt] += red[(w * NT + tt) * 64 + lane];
+        if (S == 1) {
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) st8_if(in_t(tt), bf16_quad(acc[tt]), cr, c_off(tile, tt));
+          continue;
+        }
+        finish_stage();
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, acc[tt]), pr, p_off(rank, tile, tt));
+        st_tile = tile;
+      }
+      stamp[2] = stamp[3] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
+      for (int f = 0; f < 3; ++f) finish_stage();  // drain: finish the last tiles
+      write_stamps();
+      return;
+    }
+  }
+
+  // ---- streaming waves ----------------------------------------------------
   f32x4 acc[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const u32x4 (&a)[LOADS], uint32_t sc, int i) {
-    const int j = wk + WK * i;
+    const int j = sw + SWK * i;
 #pragma unroll
     for (int s2 = 0; s2 < SUBS; ++s2) {
       bf16x8 b[NT];
@@ -470,15 +609,17 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_stream_kernel(GemmParams 
     }
   };
 
-  const rsrc_t cr = make_rsrc(p.c, (uint32_t)T * (uint32_t)N * 2u);
-  const rsrc_t pr = make_rsrc(p.part, (uint32_t)S * (uint32_t)T * (uint32_t)N * 4u);
-
-  // End of one tile: wave-order sum through LDS (WK > 1), then the column's
-  // wave 0 stores.
+  // End of one tile for a streaming wave.
   auto tile_end = [&](int k) {
     const int tile = col + cstride * k;
-    if constexpr (WK > 1) {
-      f32x4* red = reinterpret_cast<f32x4*>(red_base) + (k & 1) * RED_QUADS;
+    f32x4* red = red_base + (k & 1) * RED_QUADS;
+    bool storer = true;
+    if constexpr (EPI) {
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) red[(sw * NT + tt) * 64 + lane] = acc[tt];
+      __syncthreads();
+      storer = false;
+    } else if constexpr (WK > 1) {
       if (wk > 0) {
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) red[((wk - 1) * NT + tt) * 64 + lane] = acc[tt];
@@ -490,19 +631,15 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_stream_kernel(GemmParams 
 #pragma unroll
           for (int tt = 0; tt < NT; ++tt) acc[tt] += red[((w - 1) * NT + tt) * 64 + lane];
       }
+      storer = (wk == 0);
     }
-    if (wk == 0) {
-      const uint32_t n = (uint32_t)(tile * 16 + 4 * g);
+    if (storer) {
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
-        const uint32_t t = (uint32_t)(tt * 16 + li);
-        const bool ok = (int)t < T;
-        if (S == 1) {
-          st8_if(ok, bf16_quad(acc[tt]), cr, (t * (uint32_t)N + n) * 2u);
-        } else {
-          st16_coherent_if(ok, __builtin_bit_cast(u32x4, acc[tt]), pr,
-                           (((uint32_t)rank * (uint32_t)T + t) * (uint32_t)N + n) * 4u);
-        }
+        if (S == 1)
+          st8_if(in_t(tt), bf16_quad(acc[tt]), cr, c_off(tile, tt));
+        else
+          st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, acc[tt]), pr, p_off(rank, tile, tt));
       }
     }
 #pragma unroll
@@ -535,49 +672,72 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_stream_kernel(GemmParams 
       consumed();
     }
   }
-  // A wave with no steps (slice shorter than WK steps) still takes part in
-  // every tile's reduction barrier.
+  // A streaming wave with no steps (slice shorter than the wave count)
+  // still takes part in every tile's barrier.
   if (n_i == 0) {
     for (int k = 0; k < ntl; ++k) tile_end(k);
   }
+  stamp[2] = stamp[3] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
+  if (EPI || S == 1) {
+    write_stamps();
+    return;
+  }
 
-  if (S == 1) return;
-
-  // ---- deferred split-K hand-off -----------------------------------------
+  // ---- deferred hand-off ----------------------------------------------------
   wait_vmem_all();  // this wave's partial stores are complete (coherent)
+  if (p.stamps) stamp[3] = __builtin_amdgcn_s_memrealtime();
   int k0 = 0, kstep = 1;
   if constexpr (WK > 1) {
-    __syncthreads();  // column wave 0's stores, seen by every wave of the column
+    __syncthreads();  // wave 0's stores, seen by every wave of the workgroup
     k0 = wk;
     kstep = WK;
   }
-  for (int k = k0; k < ntl; k += kstep) {
-    const int tile = col + cstride * k;
-    uint32_t old = 0;
-    if (lane == 0)
-      old = __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    if (old != (uint32_t)(S - 1)) continue;
-    if (lane == 0) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // Last rank on this tile: partials of ranks 0..S-1 summed in rank order.
-    const uint32_t n = (uint32_t)(tile * 16 + 4 * g);
+  const int my_tiles = (ntl > k0) ? (ntl - k0 + kstep - 1) / kstep : 0;
+  auto tile_of = [&](int j) { return col + cstride * (k0 + kstep * j); };
+  for (int j0 = 0; j0 < my_tiles; j0 += 64) {
+    const int j = j0 + lane;
+    bool last = false;
+    if (j < my_tiles) {
+      const int tile = tile_of(j);
+      const uint32_t old =
+          __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = (old == (uint32_t)(S - 1));
+      if (last) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    uint64_t mask = __builtin_amdgcn_ballot_w64(last);
+    while (mask) {
+      const int b0 = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      const int b1 = mask ? __builtin_ctzll(mask) : -1;
+      if (b1 >= 0) mask &= mask - 1;
+      const int t0 = tile_of(j0 + b0);
+      const int t1 = tile_of(j0 + (b1 >= 0 ? b1 : b0));
 #pragma unroll 1
-    for (int tt = 0; tt < NT; ++tt) {
-      const uint32_t t = (uint32_t)(tt * 16 + li);
-      const bool ok = (int)t < T;
-      f32x4 v[8];
+      for (int tt = 0; tt < NT; ++tt) {
+        const bool ok = in_t(tt);
+        const bool ok1 = ok && b1 >= 0;
+        f32x4 v0[8], v1[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        if (r < S)
-          v[r] = __builtin_bit_cast(
-              f32x4, ld16_coherent_if(ok, pr, (((uint32_t)r * (uint32_t)T + t) * (uint32_t)N + n) * 4u));
-      f32x4 tot = v[0];
+        for (int r = 0; r < 8; ++r) {
+          if (r < S) {
+            v0[r] = __builtin_bit_cast(f32x4, ld16_coherent_if(ok, pr, p_off(r, t0, tt)));
+            v1[r] = __builtin_bit_cast(f32x4, ld16_coherent_if(ok1, pr, p_off(r, t1, tt)));
+          }
+        }
+        f32x4 s0 = v0[0], s1 = v1[0];
 #pragma unroll
-      for (int r = 1; r < 8; ++r)
-        if (r < S) tot += v[r];
-      st8_if(ok, bf16_quad(tot), cr, (t * (uint32_t)N + n) * 2u);
+        for (int r = 1; r < 8; ++r) {
+          if (r < S) {
+            s0 += v0[r];
+            s1 += v1[r];
+          }
+        }
+        st8_if(ok, bf16_quad(s0), cr, c_off(t0, tt));
+        st8_if(ok1, bf16_quad(s1), cr, c_off(t1, tt));
+      }
     }
   }
+  write_stamps();
 }
 
 // ---------------------------------------------------------------------------
@@ -701,15 +861,15 @@ bool shape_fits(int si, int T, int N, int ks, int S, bool mx, Tactic* t) {
 // ---- persistent stream kernel configurations --------------------------
 
 struct StreamShape {
-  int wk, wn, d, c;
+  int wk, wn, d, c, epi;
 };
 constexpr StreamShape kStreamShapes[] = {
-    {1, 8, 8, 2},  // 0: 8 waves, each streaming its own tiles
-    {1, 8, 8, 1},  // 1
-    {1, 4, 8, 2},  // 2
-    {8, 1, 8, 2},  // 3: 8 waves share each tile's K slice (LDS wave-order sum)
-    {8, 1, 8, 1},  // 4
-    {4, 1, 8, 1},  // 5
+    {8, 1, 8, 2, 0},  // 0: 8 waves share each tile's K slice, deferred hand-off
+    {8, 1, 8, 1, 0},  // 1
+    {8, 1, 8, 2, 1},  // 2: 7 streaming waves + an epilogue wave (pipelined hand-off)
+    {8, 1, 8, 1, 1},  // 3
+    {4, 1, 8, 1, 0},  // 4
+    {1, 8, 8, 2, 0},  // 5: 8 waves, each streaming its own tiles
 };
 constexpr int kNumStreamShapes = sizeof(kStreamShapes) / sizeof(kStreamShapes[0]);
 constexpr int kStreamMaxNT = 2;
@@ -718,7 +878,7 @@ constexpr int kStreamMaxX = 128 * 1024;
 template <int NT, int SH, bool MX>
 hipError_t launch_stream_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
   constexpr StreamShape sh = kStreamShapes[SH];
-  auto kern = splitk_stream_kernel<NT, sh.wk, sh.wn, sh.d, sh.c, MX>;
+  auto kern = splitk_stream_kernel<NT, sh.wk, sh.wn, sh.d, sh.c, sh.epi != 0, MX>;
   hipLaunchKernelGGL(kern, dim3(t.grid), dim3(t.threads), t.lds, s, p);
   return hipGetLastError();
 }
@@ -757,18 +917,21 @@ bool stream_fits(int si, int T, int N, int ks, int S, bool mx, Tactic* t) {
   const int step = mx ? 128 : 32 * c.c;
   if (ks % step) return false;
   const int cs = ks / step;
-  if (cs < c.wk) return false;  // every wave needs at least one step per tile
+  const int streaming = c.epi ? c.wk - 1 : c.wk;
+  if (cs < streaming) return false;  // every streaming wave needs a step per tile
   const long x_lds = (long)T * ks * 2;
   if (x_lds > kStreamMaxX) return false;
-  const int red = c.wk > 1 ? 2 * (c.wk - 1) * t->nt * 64 * 16 : 0;
+  const int parked = c.epi ? c.wk - 1 : c.wk - 1;  // sums parked in LDS per tile
+  const int red = c.wk > 1 ? 2 * parked * t->nt * 64 * 16 : 0;
   const long lds = x_lds + red;
   if (lds > kMaxLds) return false;
   const int n_tiles = N / 16;
-  // Resident workgroups per CU: LDS-bound, at most 32 waves per CU.
+  // Resident workgroups per CU: LDS-bound and the register budget the kernel
+  // is built with.
   const int waves = c.wk * c.wn;
   int per_cu = (int)((160L * 1024) / (lds > 0 ? lds : 1));
-  if (per_cu > 32 / waves) per_cu = 32 / waves;
-  per_cu = env_int("SKGEMM_WG_PER_CU", per_cu < 2 ? per_cu : 2);
+  if (per_cu > stream_wgs_per_cu(t->nt)) per_cu = stream_wgs_per_cu(t->nt);
+  per_cu = env_int("SKGEMM_WG_PER_CU", per_cu);
   if (per_cu < 1) per_cu = 1;
   long g = (256L * per_cu) / S;
   const long g_max = (n_tiles + c.wn - 1) / c.wn;  // every column gets a tile
@@ -810,8 +973,23 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
       // Eight waves share each tile's K slice (measured fastest on the decode
       // shapes: 16 weight rows open per workgroup, 8 streams on them); the
       // one-wave-per-tile shapes remain for when the slice is too short.
-      static const int pref[] = {3, 4, 5, 0, 1, 2};
-      for (int si : pref) {
+      // With few tiles per workgroup the hand-off is most of the tail, and a
+      // dedicated epilogue wave that overlaps it with the stream wins; with
+      // many tiles all eight waves streaming wins.
+      static const int many[] = {0, 1, 2, 3, 4, 5};
+      static const int few[] = {2, 3, 0, 1, 4, 5};
+      const int* pref = many;
+      for (int si : many) {
+        Tactic probe = t;
+        if (stream_fits(si, tr, N, ks, S, mx, &probe)) {
+          const int groups = probe.grid / S;
+          const int per_wg = (N / 16 + groups - 1) / groups;
+          if (per_wg <= 4) pref = few;
+          break;
+        }
+      }
+      for (int oi = 0; oi < kNumStreamShapes; ++oi) {
+        const int si = pref[oi];
         if (stream_fits(si, tr, N, ks, S, mx, &t)) {
           *out = t;
           return true;

@@ -18,6 +18,7 @@ struct GemmParams {
   int ks;       // K / S: the K slice of one split rank
   int kc;       // K elements of X staged in LDS at a time; divides ks
   int nchunks;  // ks / kc
+  uint64_t* stamps;  // optional per-workgroup phase stamps (stream kernel)
 };
 
 // A kernel configuration. One workgroup computes a TILE_N x T tile over one K

@@ -274,3 +274,31 @@ def test_every_kernel_shape(var, val, monkeypatch):
         log(f"forced {var}={val}: mxfp4 T={T} N={N} K={K} S={S} tactic={tac}")
         x, wq, ws = workloads.small_mxfp4_case(T, K, N, seed=6000 + T + S)
         assert_parity(run_mxfp4(x, wq, ws, S), G.gemm_mxfp4_ref(x, wq, ws), K, f"{var}={val} mx T={T}")
+
+
+def test_timeline_stamps():
+    """Opt-in phase stamps: five non-decreasing device-clock values per
+    workgroup, results unchanged, and nothing written once turned off."""
+    t = torch()
+    w = workloads.WORKLOADS["bf16_t8_k7168_n2048"]
+    x = workloads.gen_x(w)
+    wb = workloads.gen_w_bf16(w)
+    tac = sk.skgemm_tactic_for(w.T, w.N, w.K, w.split_k)
+    log(f"timeline stamps on {w.name}, tactic={tac}")
+    assert tac["kind"] == "stream"
+    buf = t.zeros(tac["grid"] * 8, dtype=t.int64, device=DEV)
+    sk.skgemm_set_timeline(buf, buf.numel())
+    try:
+        c = run_bf16(x, wb, w.split_k)
+    finally:
+        sk.skgemm_set_timeline(None, 0)
+    st = buf.view(tac["grid"], 8).cpu().numpy()
+    assert np.all(st[:, :5] > 0) and np.all(st[:, 5:] == 0)
+    assert np.all(np.diff(st[:, :5], axis=1) >= 0)
+    span_us = (st[:, 4].max() - st[:, 0].min()) * 0.01
+    log(f"  workgroup span {span_us:.2f} us")
+    assert 0 < span_us < 1e4
+    assert_parity(c, G.gemm_bf16_ref(x, wb), w.K, "with stamps")
+    buf.zero_()
+    run_bf16(x, wb, w.split_k)
+    assert int(buf.abs().sum().item()) == 0
