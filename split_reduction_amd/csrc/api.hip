@@ -2,6 +2,7 @@
 // blocking and kernel dispatch. Declarations and contracts: include/skgemm.h.
 
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -20,6 +21,15 @@ constexpr int kTokenBlock = 128;  // rows of X / C per launch (16 * 8 MFMA tiles
 thread_local int g_last_hip_error = 0;
 
 // Optional phase-stamp buffer (skgemm_set_timeline).
+// How long a tile's owner waits for the other split ranks before handing the
+// tile to the last to arrive: 100 us of the 100 MHz device clock, unless
+// SKGEMM_OWNER_WAIT gives another tick count (tests set 0 to exercise the
+// hand-over path).
+uint32_t owner_wait_ticks() {
+  const char* e = getenv("SKGEMM_OWNER_WAIT");
+  return e ? (uint32_t)strtoul(e, nullptr, 10) : 10000u;
+}
+
 std::atomic<uint64_t*> g_stamps{nullptr};
 std::atomic<size_t> g_stamps_cap{0};
 
@@ -138,6 +148,7 @@ int run_gemm(bool mx, const void* w, const void* ws, const void* x, void* c, int
     p.kc = tac.kc;
     p.nchunks = (tac.kc > 0) ? p.ks / tac.kc : 0;
     p.stamps = ((size_t)tac.grid * 8 <= g_stamps_cap.load()) ? g_stamps.load() : nullptr;
+    p.owner_wait = owner_wait_ticks();
     hipError_t e = skg::launch_gemm(tac, p, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -228,9 +239,10 @@ SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int mxfp4, ch
     snprintf(buf, buf_len,
              "{\"nt\": %d, \"rg\": %d, \"wk\": %d, \"wn\": %d, \"d\": %d, \"c\": %d, \"kc\": %d, "
              "\"tile_n\": %d, \"threads\": %d, \"lds\": %d, \"grid\": %d, \"split_k\": %d, "
-             "\"token_blocks\": %d, \"mxfp4\": %d, \"kind\": \"%s\", \"shape\": %d}",
+             "\"token_blocks\": %d, \"mxfp4\": %d, \"kind\": \"%s\", \"shape\": %d, \"fold\": %d}",
              t.nt, t.rg, t.wk, t.wn, t.d, t.c, t.kc, t.tile_n, t.threads, t.lds, t.grid, split_k,
-             blocks, t.mx, t.kind == 1 ? "stream" : "tiled", t.shape);
+             blocks, t.mx, t.kind == 2 ? "cluster" : (t.kind == 1 ? "stream" : "tiled"), t.shape,
+             t.kind == 2 ? t.fold : 1);
   }
   return SKGEMM_OK;
 }

@@ -112,10 +112,11 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
     srow_off[rg] = row * (uint32_t)(K / 32);
   }
   // Byte offset, within a weight row, of this lane's first piece of a step
-  // starting at K element kel: bf16 pieces c cover K elements
-  // kel + 8C*g + 8c .. +7; an MXFP4 lane covers kel + 32g .. +31.
+  // starting at K element kel: bf16 piece c covers K elements
+  // kel + 32c + 8g .. +7 (one load instruction reads 64 contiguous bytes of
+  // each row); an MXFP4 lane covers kel + 32g .. +31.
   auto w_lane_off = [&](int kel) -> uint32_t {
-    return MX ? (uint32_t)(kel / 2 + 16 * g) : (uint32_t)(kel * 2 + 16 * C * g);
+    return MX ? (uint32_t)(kel / 2 + 16 * g) : (uint32_t)(kel * 2 + 16 * g);
   };
 
   f32x4 acc[RG][NT];
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
 #pragma unroll
       for (int rg = 0; rg < RG; ++rg) {
 #pragma unroll
-        for (int l = 0; l < LOADS; ++l) ring[slot_s][rg][l] = ld16_if(ok, wr, row_off[rg] + lo + 16 * l);
+        for (int l = 0; l < LOADS; ++l) ring[slot_s][rg][l] = ld16_if(ok, wr, row_off[rg] + lo + 64 * l);
         if constexpr (MX) sring[slot_s][rg] = ld1_if(ok, sr, srow_off[rg] + kel / 32 + g);
       }
     };
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
             if constexpr (MX) {
               j = k / 128; gg = (k % 128) / 32; s = (k % 32) / 8;
             } else {
-              j = k / (32 * C); gg = (k % (32 * C)) / (8 * C); s = (k % (8 * C)) / 8;
+              j = k / (32 * C); s = (k % (32 * C)) / 32; gg = (k % 32) / 8;
             }
             lds_write16(smem, x_slot(j, s, gg, t), v[b]);
           }
@@ -427,9 +428,9 @@ void splitk_stream_kernel(GemmParams p) {
   auto issue = [&](int slot) {
     const bool ok = issued < total;
     const int kel = kbase + (sw + SWK * pf_i) * STEP_K;
-    const uint32_t lo = MX ? (uint32_t)(kel / 2 + 16 * g) : (uint32_t)(kel * 2 + 16 * C * g);
+    const uint32_t lo = MX ? (uint32_t)(kel / 2 + 16 * g) : (uint32_t)(kel * 2 + 16 * g);
 #pragma unroll
-    for (int l = 0; l < LOADS; ++l) ring[slot][l] = ld16_if(ok, wr, pf_row + lo + 16 * l);
+    for (int l = 0; l < LOADS; ++l) ring[slot][l] = ld16_if(ok, wr, pf_row + lo + 64 * l);
     if constexpr (MX) sring[slot] = ld1_if(ok, sr, pf_srow + (uint32_t)(kel / 32 + g));
     ++issued;
     if (++pf_i == n_i) {
@@ -443,13 +444,23 @@ void splitk_stream_kernel(GemmParams p) {
   // The first batch of X loads goes out before the weight prologue, so its
   // LDS writes wait only for X (loads complete in issue order) and the
   // multiplies can start while the weights are still arriving.
+  // Workgroups of one rank that share an XCD stage the same slice at the same
+  // time; each starts at a different point of it (a rotation of the piece
+  // order) so that their requests for the same lines do not queue on one L2
+  // channel together.
   const int pieces = T * (p.ks / 8);
+  const int rot = (int)(((unsigned)gi % 32u) * (unsigned)(pieces / 32));
+  auto piece = [&](int pc) -> int {
+    const int q = pc + rot;
+    return q >= pieces ? q - pieces : q;
+  };
   auto stage_load = [&](int p0, u32x4 (&v)[XBATCH]) {
 #pragma unroll
     for (int b = 0; b < XBATCH; ++b) {
       const int pc = p0 + b * THREADS;
-      const int t = pc % T;
-      const int k = (pc / T) * 8;
+      const int q = piece(pc);
+      const int t = q % T;
+      const int k = (q / T) * 8;
       v[b] = ld16_if(pc < pieces, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(kbase + k)) * 2u);
     }
   };
@@ -458,13 +469,14 @@ void splitk_stream_kernel(GemmParams p) {
     for (int b = 0; b < XBATCH; ++b) {
       const int pc = p0 + b * THREADS;
       if (pc < pieces) {
-        const int t = pc % T;
-        const int k = (pc / T) * 8;
+        const int q = piece(pc);
+        const int t = q % T;
+        const int k = (q / T) * 8;
         int j, s2, gg;
         if constexpr (MX) {
           j = k / 128; gg = (k % 128) / 32; s2 = (k % 32) / 8;
         } else {
-          j = k / (32 * C); gg = (k % (32 * C)) / (8 * C); s2 = (k % (8 * C)) / 8;
+          j = k / (32 * C); s2 = (k % (32 * C)) / 32; gg = (k % 32) / 8;
         }
         lds_write16(smem, x_slot(j, s2, gg, t), v[b]);
       }
@@ -684,6 +696,15 @@ void splitk_stream_kernel(GemmParams p) {
   }
 
   // ---- deferred hand-off ----------------------------------------------------
+  // The k-th tile of a list has an owner rank, (k + gi) mod S, the same in
+  // every rank of the group, so the reductions spread evenly over the ranks
+  // (and over the XCDs, which the ranks map to). Every rank bumps the tile's
+  // arrival counter once its partial stores are complete. The owner waits,
+  // for a bounded time, until all S have arrived, then sums the partials in
+  // rank order, stores C and clears the counter. If the wait runs out (a
+  // peer that is not resident, e.g. under a concurrent kernel), the owner sets
+  // the abandon bit and the last rank to arrive finishes the tile instead, so
+  // the result never depends on the peers being resident.
   wait_vmem_all();  // this wave's partial stores are complete (coherent)
   if (p.stamps) stamp[3] = __builtin_amdgcn_s_memrealtime();
   int k0 = 0, kstep = 1;
@@ -692,50 +713,101 @@ void splitk_stream_kernel(GemmParams p) {
     k0 = wk;
     kstep = WK;
   }
-  const int my_tiles = (ntl > k0) ? (ntl - k0 + kstep - 1) / kstep : 0;
-  auto tile_of = [&](int j) { return col + cstride * (k0 + kstep * j); };
-  for (int j0 = 0; j0 < my_tiles; j0 += 64) {
-    const int j = j0 + lane;
-    bool last = false;
-    if (j < my_tiles) {
-      const int tile = tile_of(j);
-      const uint32_t old =
-          __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = (old == (uint32_t)(S - 1));
-      if (last) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  constexpr uint32_t kArrivals = 0xFFu;  // arrival count bits of a counter
+  constexpr uint32_t kAbandon = 0x100u;  // the owner stopped waiting
+  auto tile_at = [&](int k) { return col + cstride * k; };
+  auto owner_of = [&](int k) { return (k + gi) % S; };
+
+  // Sums the S partials of tile t0 (and t1 >= 0) in rank order, one store.
+  auto finish = [&](int t0, int t1) {
+    const int t1c = t1 >= 0 ? t1 : t0;
+#pragma unroll 1
+    for (int tt = 0; tt < NT; ++tt) {
+      const bool ok = in_t(tt);
+      const bool ok1 = ok && t1 >= 0;
+      f32x4 v0[8], v1[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        if (r < S) {
+          v0[r] = __builtin_bit_cast(f32x4, ld16_coherent_if(ok, pr, p_off(r, t0, tt)));
+          v1[r] = __builtin_bit_cast(f32x4, ld16_coherent_if(ok1, pr, p_off(r, t1c, tt)));
+        }
+      }
+      f32x4 s0 = v0[0], s1 = v1[0];
+#pragma unroll
+      for (int r = 1; r < 8; ++r) {
+        if (r < S) {
+          s0 += v0[r];
+          s1 += v1[r];
+        }
+      }
+      st8_if(ok, bf16_quad(s0), cr, c_off(t0, tt));
+      st8_if(ok1, bf16_quad(s1), cr, c_off(t1c, tt));
     }
-    uint64_t mask = __builtin_amdgcn_ballot_w64(last);
+  };
+  // Finishes the tiles of the lanes set in `mask`, two at a time.
+  auto finish_mask = [&](uint64_t mask, auto tile_of_lane) {
     while (mask) {
       const int b0 = __builtin_ctzll(mask);
       mask &= mask - 1;
       const int b1 = mask ? __builtin_ctzll(mask) : -1;
       if (b1 >= 0) mask &= mask - 1;
-      const int t0 = tile_of(j0 + b0);
-      const int t1 = tile_of(j0 + (b1 >= 0 ? b1 : b0));
-#pragma unroll 1
-      for (int tt = 0; tt < NT; ++tt) {
-        const bool ok = in_t(tt);
-        const bool ok1 = ok && b1 >= 0;
-        f32x4 v0[8], v1[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          if (r < S) {
-            v0[r] = __builtin_bit_cast(f32x4, ld16_coherent_if(ok, pr, p_off(r, t0, tt)));
-            v1[r] = __builtin_bit_cast(f32x4, ld16_coherent_if(ok1, pr, p_off(r, t1, tt)));
-          }
-        }
-        f32x4 s0 = v0[0], s1 = v1[0];
-#pragma unroll
-        for (int r = 1; r < 8; ++r) {
-          if (r < S) {
-            s0 += v0[r];
-            s1 += v1[r];
-          }
-        }
-        st8_if(ok, bf16_quad(s0), cr, c_off(t0, tt));
-        st8_if(ok1, bf16_quad(s1), cr, c_off(t1, tt));
-      }
+      finish(tile_of_lane(b0), b1 >= 0 ? tile_of_lane(b1) : -1);
     }
+  };
+
+  // Arrivals: this wave's share of the list, a lane per tile.
+  const int my_tiles = (ntl > k0) ? (ntl - k0 + kstep - 1) / kstep : 0;
+  for (int j0 = 0; j0 < my_tiles; j0 += 64) {
+    const int j = j0 + lane;
+    bool take = false;
+    if (j < my_tiles) {
+      const int k = k0 + kstep * j;
+      const int tile = tile_at(k);
+      const uint32_t old =
+          __hip_atomic_fetch_add(p.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // Last to arrive at a tile its owner gave up on: finish it here.
+      take = owner_of(k) != rank && (old & kAbandon) != 0 && (old & kArrivals) == (uint32_t)(S - 1);
+      if (take) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    finish_mask(__builtin_amdgcn_ballot_w64(take),
+                [&](int b) { return tile_at(k0 + kstep * (j0 + b)); });
+  }
+
+  // Owned tiles: k = k_first + S*m, m spread over the waves like the list.
+  const int k_first = ((rank - gi) % S + S) % S;
+  const int n_own = (ntl > k_first) ? (ntl - k_first + S - 1) / S : 0;
+  const int my_own = (n_own > k0) ? (n_own - k0 + kstep - 1) / kstep : 0;
+  auto own_k = [&](int i) { return k_first + S * (k0 + kstep * i); };
+  for (int i0 = 0; i0 < my_own; i0 += 64) {
+    const int i = i0 + lane;
+    const bool mine = i < my_own;
+    const int tile = mine ? tile_at(own_k(i)) : 0;
+    bool pending = mine;
+    bool ready = false;
+    const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + p.owner_wait;
+    while (true) {
+      if (pending) {
+        const uint32_t v = __hip_atomic_load(p.cnt + tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((v & kArrivals) == (uint32_t)S) {
+          ready = true;
+          pending = false;
+        }
+      }
+      if (__builtin_amdgcn_ballot_w64(pending) == 0) break;
+      if (__builtin_amdgcn_s_memrealtime() > deadline) {
+        if (pending) {
+          const uint32_t old = __hip_atomic_fetch_or(p.cnt + tile, kAbandon, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+          ready = (old & kArrivals) == (uint32_t)S;  // all arrived meanwhile: still ours
+          pending = false;
+        }
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (ready) __hip_atomic_store(p.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    finish_mask(__builtin_amdgcn_ballot_w64(ready), [&](int b) { return tile_at(own_k(i0 + b)); });
   }
   write_stamps();
 }
@@ -874,6 +946,7 @@ constexpr StreamShape kStreamShapes[] = {
 constexpr int kNumStreamShapes = sizeof(kStreamShapes) / sizeof(kStreamShapes[0]);
 constexpr int kStreamMaxNT = 2;
 constexpr int kStreamMaxX = 128 * 1024;
+constexpr int kClusterMaxGrid = 512;
 
 template <int NT, int SH, bool MX>
 hipError_t launch_stream_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
@@ -961,9 +1034,26 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
   const int ks = K / S;
   const int tr = T > 0 ? T : 1;
 
-  // Persistent streaming kernel first (SKGEMM_STREAM=-1 disables it,
+  // SKGEMM_KIND=<0|1|2> restricts the choice to one kernel kind (tuning runs);
+  // SKGEMM_FOLD and SKGEMM_CLUSTER_C cap the fold and pin the pieces per lane
+  // of kind 2.
+  const int kind = env_int("SKGEMM_KIND", -1);
+  if (kind == 2 || kind < 0) {
+    Tactic c = t;
+    if (cluster_fits(tr, N, ks, S, mx, env_int("SKGEMM_FOLD", 8), env_int("SKGEMM_CLUSTER_C", 0), &c)) {
+      // Whole tiles per workgroup pay off while the grid is about one
+      // workgroup per CU; beyond, the persistent kernel's staged activations
+      // and amortised ramp-up win.
+      if (kind == 2 || c.grid <= kClusterMaxGrid) {
+        *out = c;
+        return true;
+      }
+    }
+    if (kind == 2) return false;
+  }
+  // Persistent streaming kernel (SKGEMM_STREAM=-1 disables it,
   // SKGEMM_STREAM=<index> forces one of its shapes, for tuning runs).
-  {
+  if (kind == 1 || kind < 0) {
     const int forced = env_int("SKGEMM_STREAM", -2);
     if (forced >= 0 && forced < kNumStreamShapes && stream_fits(forced, tr, N, ks, S, mx, &t)) {
       *out = t;
@@ -997,6 +1087,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
       }
     }
   }
+  if (kind == 1) return false;
   // A tiled shape forced for tuning runs (SKGEMM_SHAPE=<index>), if it fits.
   if (const char* e = getenv("SKGEMM_SHAPE")) {
     const int si = atoi(e);
@@ -1021,6 +1112,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
 }
 
 hipError_t launch_gemm(const Tactic& t, const GemmParams& p, hipStream_t s) {
+  if (t.kind == 2) return launch_cluster(t, p, s);
   if (t.kind == 1) return t.mx ? launch_stream_fmt<true>(t.shape, t, p, s)
                                : launch_stream_fmt<false>(t.shape, t, p, s);
   const int sh = shape_index(t);

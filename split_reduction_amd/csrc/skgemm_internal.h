@@ -18,7 +18,10 @@ struct GemmParams {
   int ks;       // K / S: the K slice of one split rank
   int kc;       // K elements of X staged in LDS at a time; divides ks
   int nchunks;  // ks / kc
-  uint64_t* stamps;  // optional per-workgroup phase stamps (stream kernel)
+  uint64_t* stamps;  // optional per-workgroup phase stamps
+  uint32_t owner_wait;  // stream kernel: device-clock ticks (100 MHz) a tile's
+                        // owner waits for the other ranks before handing the
+                        // tile to the last to arrive
 };
 
 // A kernel configuration. One workgroup computes a TILE_N x T tile over one K
@@ -39,13 +42,21 @@ struct Tactic {
   int lds;      // dynamic LDS bytes
   int grid;     // workgroups = (N / tile_n) * split_k
   int mx;       // 1 for MXFP4 weights
-  int kind;     // 0: one tile per workgroup; 1: persistent stream kernel
+  int kind;     // 0: one tile per workgroup; 1: persistent stream kernel;
+                // 2: all split ranks of a tile in one workgroup
   int shape;    // index into the kind's shape table
+  int fold;     // kind 2: K windows folded into one MFMA operand (tile rows 16/fold)
 };
 
 // Picks the configuration for a launch over T <= 128 rows; returns false if no
 // instantiated configuration fits (never for validated shapes).
 bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out);
+
+// Fills the configuration of the one-workgroup-per-tile kernel (kind 2) for a
+// launch over T <= 32 rows, folding at most max_fold ways (force_c > 0 pins
+// the pieces per lane for bf16); false if it does not apply.
+bool cluster_fits(int T, int N, int ks, int S, bool mx, int max_fold, int force_c, Tactic* t);
+hipError_t launch_cluster(const Tactic& t, const GemmParams& p, hipStream_t stream);
 
 // Enqueues one launch (T <= 128). Returns the launch's hipError_t.
 hipError_t launch_gemm(const Tactic& tac, const GemmParams& p, hipStream_t stream);

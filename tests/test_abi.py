@@ -101,6 +101,11 @@ def test_tactics_cover_the_workloads(T, N, K, S, mx):
     assert N % t["tile_n"] == 0
     if t["kind"] == "tiled":
         assert t["grid"] == (N // t["tile_n"]) * S
+    elif t["kind"] == "cluster":  # one workgroup per tile of 16/fold rows, S rank groups of waves
+        assert t["tile_n"] * t["fold"] == 16 and t["grid"] == N // t["tile_n"]
+        assert t["threads"] % (64 * S) == 0 and t["threads"] <= 1024
+        assert T <= 16 // t["fold"] or (t["fold"] == 1 and T <= 32)
+        assert t["kc"] == K // S and t["lds"] == 0
     else:  # persistent: G workgroups per split rank, every wave column owns a tile
         assert t["grid"] % S == 0 and t["tile_n"] == 16
         assert 1 <= (t["grid"] // S - 1) * t["wn"] < N // 16

@@ -256,29 +256,99 @@ def test_graph_replays_match_eager():
 # tactic reads (SKGEMM_STREAM selects a persistent-kernel shape or -1 to turn
 # it off, SKGEMM_SHAPE a one-tile-per-workgroup shape), on shapes with ragged
 # T, uneven step counts per wave and several tiles per wave column.
-FORCED = [("SKGEMM_STREAM", str(i)) for i in range(6)] + [("SKGEMM_SHAPE", str(i)) for i in range(6)]
+FORCED = (
+    [{"SKGEMM_KIND": "1", "SKGEMM_STREAM": str(i)} for i in range(6)]
+    + [{"SKGEMM_KIND": "0", "SKGEMM_SHAPE": str(i)} for i in range(6)]
+    + [{"SKGEMM_KIND": "2", "SKGEMM_FOLD": str(f), "SKGEMM_CLUSTER_C": str(c)}
+       for f in (1, 2, 4, 8) for c in (1, 2)]
+)
 
 
-@pytest.mark.parametrize("var,val", FORCED)
-def test_every_kernel_shape(var, val, monkeypatch):
-    if var == "SKGEMM_SHAPE":
-        monkeypatch.setenv("SKGEMM_STREAM", "-1")
-    monkeypatch.setenv(var, val)
-    for (T, N, K, S) in [(3, 512, 1792, 4), (24, 1024, 2048, 8), (17, 256, 7168, 2), (1, 4096, 512, 1)]:
-        tac = sk.skgemm_tactic_for(T, N, K, S)
-        log(f"forced {var}={val}: bf16 T={T} N={N} K={K} S={S} tactic={tac}")
+@pytest.mark.parametrize("env", FORCED, ids=lambda e: ",".join(f"{k[7:]}={v}" for k, v in e.items()))
+def test_every_kernel_shape(env, monkeypatch):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    kind = {"0": "tiled", "1": "stream", "2": "cluster"}[env["SKGEMM_KIND"]]
+    bf16_cases = [(3, 512, 1792, 4), (24, 1024, 2048, 8), (17, 256, 7168, 2), (1, 4096, 512, 1),
+                  (7, 96, 2048, 2), (2, 64, 1024, 8)]
+    ran = 0
+
+    def tactic(T, N, K, S, mx):
+        # A forced kind that cannot take the shape (slice too short for its
+        # waves, T beyond its token tiles) refuses it rather than falling back.
+        try:
+            return sk.skgemm_tactic_for(T, N, K, S, mx)
+        except sk.SkgemmError as e:
+            assert e.code == sk.SKGEMM_ESHAPE
+            log(f"forced {env}: T={T} N={N} K={K} S={S} mx={mx} not applicable")
+            return None
+
+    for (T, N, K, S) in bf16_cases:
+        tac = tactic(T, N, K, S, False)
+        if tac is None:
+            continue
+        log(f"forced {env}: bf16 T={T} N={N} K={K} S={S} tactic={tac}")
+        assert tac["kind"] == kind
         x, w = workloads.small_bf16_case(T, K, N, seed=5000 + T + S)
-        assert_parity(run_bf16(x, w, S), G.gemm_bf16_ref(x, w), K, f"{var}={val} T={T} S={S}")
-    for (T, N, K, S) in [(5, 512, 2048, 4), (30, 256, 1024, 2)]:
-        tac = sk.skgemm_tactic_for(T, N, K, S, True)
-        log(f"forced {var}={val}: mxfp4 T={T} N={N} K={K} S={S} tactic={tac}")
+        assert_parity(run_bf16(x, w, S), G.gemm_bf16_ref(x, w), K, f"{env} T={T} S={S}")
+        ran += 1
+    for (T, N, K, S) in [(5, 512, 2048, 4), (30, 256, 1024, 2), (1, 128, 1024, 2), (5, 512, 8192, 2),
+                         (20, 256, 2048, 1)]:
+        tac = tactic(T, N, K, S, True)
+        if tac is None:
+            continue
+        log(f"forced {env}: mxfp4 T={T} N={N} K={K} S={S} tactic={tac}")
+        assert tac["kind"] == kind
         x, wq, ws = workloads.small_mxfp4_case(T, K, N, seed=6000 + T + S)
-        assert_parity(run_mxfp4(x, wq, ws, S), G.gemm_mxfp4_ref(x, wq, ws), K, f"{var}={val} mx T={T}")
+        assert_parity(run_mxfp4(x, wq, ws, S), G.gemm_mxfp4_ref(x, wq, ws), K, f"{env} mx T={T}")
+        ran += 1
+    assert ran >= 4
 
 
-def test_timeline_stamps():
+def test_cluster_integer_exact(monkeypatch):
+    """The one-workgroup-per-tile kernel at every fold and split: integer
+    operands make every FP32 order exact, so C is the RNE of the exact sum."""
+    monkeypatch.setenv("SKGEMM_KIND", "2")
+    for f in (1, 2, 4, 8):
+        monkeypatch.setenv("SKGEMM_FOLD", str(f))
+        for (T, N, K, S) in [(1, 64, 1024, 4), (3, 32, 512, 2), (8, 48, 2048, 8), (16, 16, 256, 1),
+                             (29, 32, 1024, 4)]:
+            tac = sk.skgemm_tactic_for(T, N, K, S)
+            log(f"cluster exact fold<={f}: T={T} N={N} K={K} S={S} tactic={tac}")
+            x, w = workloads.integer_bf16_case(T, K, N, seed=7000 + 10 * f + T)
+            got = run_bf16(x, w, S)
+            exact = G.gemm_bf16_ref(x, w)
+            assert np.max(np.abs(exact)) < 2**24
+            want = F.f32_to_bf16_rne(exact.astype(np.float32))
+            assert np.array_equal(F.bf16_bits_to_f64(got), F.bf16_bits_to_f64(want)), \
+                f"fold<={f} T={T} S={S}"
+
+
+@pytest.mark.parametrize("shape", ["1", "4", "5"])
+@pytest.mark.parametrize("wait", ["0", "1", "10000"])
+def test_owner_handover(wait, shape, monkeypatch):
+    """The persistent kernel's tile owners wait as usual, give up at once, or
+    after one tick and hand their tiles to the last rank to arrive: results
+    must be unchanged, several launches in a row (the counters end each
+    launch at 0)."""
+    monkeypatch.setenv("SKGEMM_KIND", "1")
+    monkeypatch.setenv("SKGEMM_STREAM", shape)
+    monkeypatch.setenv("SKGEMM_OWNER_WAIT", wait)
+    for (T, N, K, S) in [(8, 2048, 7168, 4), (24, 1024, 2048, 8), (3, 4096, 1024, 2)]:
+        tac = sk.skgemm_tactic_for(T, N, K, S)
+        log(f"owner hand-over wait={wait}: T={T} N={N} K={K} S={S} tactic={tac}")
+        assert tac["kind"] == "stream" and tac["shape"] == int(shape)
+        x, w = workloads.small_bf16_case(T, K, N, seed=8000 + T + S)
+        ref = G.gemm_bf16_ref(x, w)
+        W = to_dev_bf16(w)
+        for rep in range(3):
+            assert_parity(run_bf16(x, None, S, W=W), ref, K, f"hand-over T={T} S={S} rep {rep}")
+
+
+def test_timeline_stamps(monkeypatch):
     """Opt-in phase stamps: five non-decreasing device-clock values per
     workgroup, results unchanged, and nothing written once turned off."""
+    monkeypatch.setenv("SKGEMM_KIND", "1")
     t = torch()
     w = workloads.WORKLOADS["bf16_t8_k7168_n2048"]
     x = workloads.gen_x(w)
