@@ -59,11 +59,20 @@ def _declare(lib):
 
 
 def lib():
-    """The loaded libskgemm.so (raises SkgemmError if it is not built)."""
+    """The loaded libskgemm.so (raises SkgemmError if it is not built).
+
+    torch is imported first: its wheel carries its own HIP runtime under the
+    same soname (libamdhip64.so.7) but loads it by file name, so if this
+    library pulled in the system runtime first, the process would hold two
+    HIP runtimes and launches from here would fail (hipErrorNoDevice). With
+    torch's runtime already loaded, this library binds to that one instance.
+    """
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise SkgemmError(SKGEMM_EHIP, f"{LIB_PATH} is not built (run split_reduction_amd/build.py)")
+        import torch  # noqa: F401  (one HIP runtime per process: torch's)
+
         try:
             handle = ctypes.CDLL(LIB_PATH)
         except OSError as e:

@@ -241,7 +241,7 @@ SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int mxfp4, ch
              "\"tile_n\": %d, \"threads\": %d, \"lds\": %d, \"grid\": %d, \"split_k\": %d, "
              "\"token_blocks\": %d, \"mxfp4\": %d, \"kind\": \"%s\", \"shape\": %d, \"fold\": %d}",
              t.nt, t.rg, t.wk, t.wn, t.d, t.c, t.kc, t.tile_n, t.threads, t.lds, t.grid, split_k,
-             blocks, t.mx, t.kind == 2 ? "cluster" : (t.kind == 1 ? "stream" : "tiled"), t.shape,
+             blocks, t.mx, t.kind == 3 ? "wide" : t.kind == 2 ? "cluster" : (t.kind == 1 ? "stream" : "tiled"), t.shape,
              t.kind == 2 ? t.fold : 1);
   }
   return SKGEMM_OK;

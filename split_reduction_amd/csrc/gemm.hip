@@ -820,18 +820,21 @@ namespace {
 
 struct Shape {
   int rg, wk, wn, d, c;
-  int max_nt;  // largest token-tile count this shape is built for
+  int max_nt;     // largest token-tile count this shape is built for (bf16)
+  int max_nt_mx;  // the same for MXFP4 weights (their decode needs registers)
 };
 
 // The instantiated workgroup shapes (each for NT = 1..8 and both weight
 // formats; MXFP4 ignores c: one 16-byte load is a whole scale block).
 constexpr Shape kShapes[] = {
-    {1, 4, 1, 8, 2, 4},  // 0: 16 rows, 4 waves along K, 2 pieces per lane per step
-    {1, 8, 1, 8, 2, 4},  // 1: 16 rows, 8 waves along K
-    {1, 8, 1, 8, 1, 4},  // 2: 16 rows, 8 waves along K, 1 piece per step
-    {2, 2, 2, 4, 1, 8},  // 3: 64 rows, two wave columns share the staged X (large T)
-    {1, 4, 2, 8, 2, 4},  // 4: 32 rows, two wave columns share the staged X
-    {1, 2, 1, 4, 1, 8},  // 5: 16 rows, any T: the fallback when no larger tile divides N
+    {1, 4, 1, 8, 2, 4, 4},  // 0: 16 rows, 4 waves along K, 2 pieces per lane per step
+    {1, 8, 1, 8, 2, 4, 4},  // 1: 16 rows, 8 waves along K
+    {1, 8, 1, 8, 1, 4, 4},  // 2: 16 rows, 8 waves along K, 1 piece per step
+    {2, 2, 2, 4, 1, 8, 8},  // 3: 64 rows, two wave columns share the staged X (large T)
+    {1, 4, 2, 8, 2, 4, 4},  // 4: 32 rows, two wave columns share the staged X
+    {1, 2, 1, 4, 1, 8, 8},  // 5: 16 rows, any T: the fallback when no larger tile divides N
+    {2, 1, 8, 4, 1, 8, 6},  // 6: 256 rows, eight wave columns share the staged X (large T)
+    {2, 1, 4, 4, 1, 8, 6},  // 7: 128 rows, four wave columns share the staged X
 };
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 
@@ -841,7 +844,7 @@ constexpr int kMaxLds = 159 * 1024;   // dynamic LDS per workgroup (160 KiB per 
 template <int NT, int SH, bool MX>
 hipError_t launch_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
   constexpr Shape sh = kShapes[SH];
-  if constexpr (NT > sh.max_nt) {
+  if constexpr (NT > (MX ? sh.max_nt_mx : sh.max_nt)) {
     return hipErrorInvalidValue;  // not built: pick_tactic never selects it
   } else {
     auto kern = splitk_gemm_kernel<NT, sh.rg, sh.wk, sh.wn, sh.d, sh.c, MX>;
@@ -859,6 +862,8 @@ hipError_t launch_nt(int sh, const Tactic& t, const GemmParams& p, hipStream_t s
     case 3: return launch_one<NT, 3, MX>(t, p, s);
     case 4: return launch_one<NT, 4, MX>(t, p, s);
     case 5: return launch_one<NT, 5, MX>(t, p, s);
+    case 6: return launch_one<NT, 6, MX>(t, p, s);
+    case 7: return launch_one<NT, 7, MX>(t, p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -903,7 +908,7 @@ int pick_kc(int ks, int step, int T) {
 // Fills the launch geometry of shape `si`; false if it does not fit.
 bool shape_fits(int si, int T, int N, int ks, int S, bool mx, Tactic* t) {
   const Shape& c = kShapes[si];
-  if (t->nt > c.max_nt) return false;
+  if (t->nt > (mx ? c.max_nt_mx : c.max_nt)) return false;
   const int tile_n = 16 * c.rg * c.wn;
   if (N % tile_n) return false;
   const int step = mx ? 128 : 32 * c.c;
@@ -1088,6 +1093,14 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
     }
   }
   if (kind == 1) return false;
+  // Many tokens: the wide-tile kernel with double-buffered X chunks.
+  if (kind == 3 || kind < 0) {
+    if (wide_fits(tr, N, ks, S, mx, &t)) {
+      *out = t;
+      return true;
+    }
+    if (kind == 3) return false;
+  }
   // A tiled shape forced for tuning runs (SKGEMM_SHAPE=<index>), if it fits.
   if (const char* e = getenv("SKGEMM_SHAPE")) {
     const int si = atoi(e);
@@ -1097,10 +1110,13 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
     }
   }
   // Preference order: up to 32 tokens, 16-row tiles with 8 waves on each
-  // (few DRAM pages open per workgroup, deep prefetch); beyond, 64-row tiles
-  // whose two wave columns share the staged activations.
-  static const int small_t[] = {1, 2, 0, 4, 3, 5};
-  static const int large_t[] = {3, 4, 1, 2, 0, 5};
+  // (few DRAM pages open per workgroup, deep prefetch); beyond, the widest
+  // tile whose wave columns share the staged activations (each workgroup
+  // reads its K range of X from L2, so wider tiles mean less of that traffic).
+  static const int small_t[] = {1, 2, 0, 4, 3, 5, 7, 6};
+  static const int large_t[] = {6, 7, 3, 4, 1, 2, 0, 5};
+  static_assert(sizeof(small_t) / sizeof(int) == kNumShapes && sizeof(large_t) / sizeof(int) == kNumShapes,
+                "every shape appears in both orders");
   const int* order = (t.nt <= 2) ? small_t : large_t;
   for (int oi = 0; oi < kNumShapes; ++oi) {
     if (shape_fits(order[oi], tr, N, ks, S, mx, &t)) {
@@ -1112,6 +1128,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
 }
 
 hipError_t launch_gemm(const Tactic& t, const GemmParams& p, hipStream_t s) {
+  if (t.kind == 3) return launch_wide(t, p, s);
   if (t.kind == 2) return launch_cluster(t, p, s);
   if (t.kind == 1) return t.mx ? launch_stream_fmt<true>(t.shape, t, p, s)
                                : launch_stream_fmt<false>(t.shape, t, p, s);

@@ -43,7 +43,8 @@ struct Tactic {
   int grid;     // workgroups = (N / tile_n) * split_k
   int mx;       // 1 for MXFP4 weights
   int kind;     // 0: one tile per workgroup; 1: persistent stream kernel;
-                // 2: all split ranks of a tile in one workgroup
+                // 2: all split ranks of a tile in one workgroup;
+                // 3: wide tiles with double-buffered X chunks (33..128 tokens)
   int shape;    // index into the kind's shape table
   int fold;     // kind 2: K windows folded into one MFMA operand (tile rows 16/fold)
 };
@@ -57,6 +58,12 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out);
 // the pieces per lane for bf16); false if it does not apply.
 bool cluster_fits(int T, int N, int ks, int S, bool mx, int max_fold, int force_c, Tactic* t);
 hipError_t launch_cluster(const Tactic& t, const GemmParams& p, hipStream_t stream);
+
+// Fills the configuration of the wide-tile kernel (kind 3) for 33 <= T <= 128
+// rows; false if it does not apply (N % 256, K slice not a whole number of
+// X chunks).
+bool wide_fits(int T, int N, int ks, int S, bool mx, Tactic* t);
+hipError_t launch_wide(const Tactic& t, const GemmParams& p, hipStream_t stream);
 
 // Enqueues one launch (T <= 128). Returns the launch's hipError_t.
 hipError_t launch_gemm(const Tactic& tac, const GemmParams& p, hipStream_t stream);

@@ -1,0 +1,387 @@
+// Split-K GEMM kernel for many tokens (T = 33..128): wide weight tiles,
+// activations staged in double-buffered K chunks.
+//
+// Same method as the other kernels (page
+// vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.gemm.splitk, module
+// summary and SplitKGemm): rank r accumulates the contiguous K slice r in
+// FP32, the ranks' partials are summed once in rank order, rounded to bf16
+// (RNE) and stored once.
+//
+// With up to 128 tokens the activation slice no longer fits in LDS, and
+// every workgroup that multiplies a weight tile must read the activations of
+// its K range from L2. That traffic is (N / rows per workgroup) * T * K * 2
+// bytes, so the tile is wide: 256 weight rows, eight waves of 32 rows each
+// (two MFMA row groups), all sharing one staged activation chunk.
+//  * X moves through LDS in chunks of KC elements, double-buffered: the loads
+//    of chunk c + 1 go out at the start of chunk c, into registers, and are
+//    written to the other buffer when chunk c is done; one barrier per chunk.
+//  * Each wave streams its 32 weight rows over the whole K slice through a
+//    D-step register ring that runs on across chunk boundaries (weights do not
+//    depend on the chunk), 16-byte buffer loads straight into MFMA A operands.
+//  * Hand-off per wave column (32 rows x T): the column's partial goes to
+//    the workspace with device-coherent stores, the wave bumps the column's
+//    arrival counter, and one owner rank per column, (column + tile) mod S,
+//    waits for the other ranks (bounded), sums the partials in rank order and
+//    stores C. An owner that runs out of time sets an abandon bit and the
+//    last rank to arrive finishes the column instead.
+
+#include "device/mfma.h"
+#include "device/mxfp4.h"
+#include "device/pack.h"
+#include "device/types.h"
+#include "skgemm_internal.h"
+
+namespace skg {
+
+namespace {
+
+constexpr int kWideWaves = 8;                // wave columns per workgroup
+constexpr int kWideRows = 32 * kWideWaves;   // weight rows per workgroup
+constexpr int wide_kc(int nt) { return nt <= 4 ? 512 : 256; }  // K elements per X chunk
+
+}  // namespace
+
+template <int NT, bool MX>
+__global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams p) {
+  constexpr int RG = 2;                       // 16-row groups per wave
+  constexpr int THREADS = 64 * kWideWaves;
+  constexpr int SUBS = MX ? 4 : 1;            // MFMA K-steps per load step
+  constexpr int STEP_K = MX ? 128 : 32;       // K elements of one load step
+  constexpr int KC = wide_kc(NT);
+  constexpr int CS = KC / STEP_K;             // load steps per chunk
+  // Ring depth in load steps (divides CS): 8 steps = 16 KiB of weights in
+  // flight per wave, 4 where the accumulators of many tokens need the registers.
+  constexpr int D = MX ? (CS < 4 ? CS : 4) : 8;
+  static_assert(CS % D == 0, "ring slots repeat every chunk");
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+  uint64_t stamp[5];  // optional phase stamps (s_memrealtime, 100 MHz)
+  stamp[0] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wn = tid >> 6;
+  const int g = lane >> 4;
+  const int li = lane & 15;
+
+  const int S = p.S;
+  const int T = p.T;
+  const int K = p.K;
+  const int N = p.N;
+  const int tile = blockIdx.x / S;
+  const int rank = blockIdx.x - tile * S;
+  const int n0 = tile * kWideRows;
+  const int kbase = rank * p.ks;
+  const int nchunks = p.ks / KC;
+  const int total = nchunks * CS;  // load steps of this wave
+
+  const uint32_t wrow_bytes = MX ? (uint32_t)(K / 2) : (uint32_t)K * 2u;
+  const rsrc_t wr = make_rsrc(static_cast<const uint8_t*>(p.w) + (size_t)n0 * wrow_bytes,
+                              (uint32_t)kWideRows * wrow_bytes);
+  const rsrc_t sr = MX ? make_rsrc(p.wscale + (size_t)n0 * (K / 32), (uint32_t)kWideRows * (uint32_t)(K / 32))
+                       : wr;
+  const rsrc_t xr = make_rsrc(p.x, (uint32_t)T * (uint32_t)K * 2u);
+
+  uint32_t row_off[RG], srow_off[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const uint32_t row = (uint32_t)((wn * RG + rg) * 16 + li);
+    row_off[rg] = row * wrow_bytes;
+    srow_off[rg] = row * (uint32_t)(K / 32);
+  }
+
+  // ---- weight ring ----------------------------------------------------------
+  u32x4 ring[D][RG];
+  uint32_t sring[D][RG];
+  auto issue = [&](int slot, int q) {
+    const bool ok = q < total;
+    const int kel = kbase + q * STEP_K;
+    const uint32_t lo = MX ? (uint32_t)(kel / 2 + 16 * g) : (uint32_t)(kel * 2 + 16 * g);
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      ring[slot][rg] = ld16_if(ok, wr, row_off[rg] + lo);
+      if constexpr (MX) sring[slot][rg] = ld1_if(ok, sr, srow_off[rg] + (uint32_t)(kel / 32 + g));
+    }
+  };
+
+  // ---- X chunks -------------------------------------------------------------
+  // Operand-ordered layout of one chunk over TP = 16 * NT token slots: slot
+  // ((j*SUBS + s)*4 + gg)*TP + t holds token t's 8 elements of load step j,
+  // sub-step s, lane K block gg. Slots of tokens t >= T hold zeros (their
+  // loads are out of range and read zero without a memory access), and every
+  // LDS offset is a compile-time constant.
+  constexpr int TP = 16 * NT;
+  constexpr int CHUNK_BYTES = TP * KC * 2;
+  constexpr int PIECES = TP * (KC / 8);
+  constexpr int XP = (PIECES + THREADS - 1) / THREADS;  // pieces per thread per chunk
+  auto x_slot = [&](int j, int s, int gg, int t) -> int { return ((j * SUBS + s) * 4 + gg) * TP + t; };
+  u32x4 xreg[XP];
+  auto x_load = [&](int c) {
+    const int k0 = kbase + c * KC;
+#pragma unroll
+    for (int b = 0; b < XP; ++b) {
+      const int pc = tid + b * THREADS;
+      const int t = pc % TP;
+      const int k = (pc / TP) * 8;
+      xreg[b] = ld16_if(pc < PIECES && t < T, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(k0 + k)) * 2u);
+    }
+  };
+  auto x_store = [&](int c) {
+    uint8_t* buf = smem + (c & 1) * CHUNK_BYTES;
+#pragma unroll
+    for (int b = 0; b < XP; ++b) {
+      const int pc = tid + b * THREADS;
+      if (PIECES % THREADS == 0 || pc < PIECES) {
+        const int t = pc % TP;
+        const int k = (pc / TP) * 8;
+        int j, s2, gg;
+        if constexpr (MX) {
+          j = k / 128; gg = (k % 128) / 32; s2 = (k % 32) / 8;
+        } else {
+          j = k / 32; s2 = 0; gg = (k % 32) / 8;
+        }
+        *reinterpret_cast<u32x4*>(buf + x_slot(j, s2, gg, t) * 16) = xreg[b];
+      }
+    }
+  };
+
+  f32x4 acc[RG][NT];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) acc[rg][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int slot, int c, int j) {
+    const uint8_t* buf = smem + (c & 1) * CHUNK_BYTES;
+#pragma unroll
+    for (int s2 = 0; s2 < SUBS; ++s2) {
+      bf16x8 b[NT];
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+        b[tt] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + x_slot(j, s2, g, tt * 16 + li) * 16));
+#pragma unroll
+      for (int rg = 0; rg < RG; ++rg) {
+        bf16x8 af;
+        if constexpr (MX) {
+          af = fp4x8_bf16(ring[slot][rg][s2], e8m0_f32(sring[slot][rg]));
+        } else {
+          af = as_bf16x8(ring[slot][rg]);
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) acc[rg][tt] = mfma_bf16(af, b[tt], acc[rg][tt]);
+      }
+    }
+  };
+
+  // Prologue: chunk 0's X first (its LDS writes then wait only for X), the
+  // weight ring behind it.
+  x_load(0);
+#pragma unroll
+  for (int s = 0; s < D; ++s) issue(s, s);
+  x_store(0);
+  __syncthreads();
+  stamp[1] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
+
+  for (int c = 0; c < nchunks; ++c) {
+    const bool next = c + 1 < nchunks;
+    if (next) x_load(c + 1);
+#pragma unroll
+    for (int j = 0; j < CS; ++j) {
+      const int slot = j % D;
+      compute(slot, c, j);
+      issue(slot, c * CS + j + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (next) {
+      x_store(c + 1);
+      __syncthreads();
+    }
+  }
+
+  stamp[2] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
+  // Thread 0 (wave 0) writes the stamps: entry, first chunk staged, weight
+  // stream done, its column's partial stored, exit.
+  auto write_stamps = [&]() {
+    if (p.stamps != nullptr && tid == 0) {
+      stamp[4] = __builtin_amdgcn_s_memrealtime();
+      const rsrc_t sr8 = make_rsrc(p.stamps + (size_t)blockIdx.x * 8, 64);
+#pragma unroll
+      for (int i = 0; i < 5; ++i)
+        st8_if(true, u32x2{(uint32_t)stamp[i], (uint32_t)(stamp[i] >> 32)}, sr8, 8u * i);
+    }
+  };
+
+  // ---- output ------------------------------------------------------------------
+  const int n_lane = n0 + wn * RG * 16 + 4 * g;  // feature of quad element 0, rg = 0
+  const rsrc_t cr = make_rsrc(p.c, (uint32_t)T * (uint32_t)N * 2u);
+  auto c_off = [&](int rg, int tt) -> uint32_t {
+    return ((uint32_t)(tt * 16 + li) * (uint32_t)N + (uint32_t)(n_lane + rg * 16)) * 2u;
+  };
+  auto in_t = [&](int tt) -> bool { return tt * 16 + li < T; };
+  if (S == 1) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt) st8_if(in_t(tt), bf16_quad(acc[rg][tt]), cr, c_off(rg, tt));
+    stamp[3] = stamp[2];
+    write_stamps();
+    return;
+  }
+
+  // ---- hand-off of this wave's column ------------------------------------------
+  const rsrc_t pr = make_rsrc(p.part, (uint32_t)S * (uint32_t)T * (uint32_t)N * 4u);
+  auto p_off = [&](int r, int rg, int tt) -> uint32_t {
+    return (((uint32_t)r * (uint32_t)T + (uint32_t)(tt * 16 + li)) * (uint32_t)N +
+            (uint32_t)(n_lane + rg * 16)) * 4u;
+  };
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
+      st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, acc[rg][tt]), pr, p_off(rank, rg, tt));
+  wait_vmem_all();  // the column's partial is complete (coherent) before it is announced
+  stamp[3] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
+
+  constexpr uint32_t kArrivals = 0xFFu;
+  constexpr uint32_t kAbandon = 0x100u;
+  uint32_t* cnt = p.cnt + (n0 / 16 + wn * RG);
+  const bool owner = (wn + tile) % S == rank;
+  uint32_t old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __builtin_amdgcn_readfirstlane(old);
+  bool finish = false;
+  if (owner) {
+    if ((old & kArrivals) == (uint32_t)(S - 1)) {
+      finish = true;  // the others were all here already
+    } else {
+      const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + p.owner_wait;
+      while (true) {
+        uint32_t v = 0;
+        if (lane == 0) v = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v = __builtin_amdgcn_readfirstlane(v);
+        if ((v & kArrivals) == (uint32_t)S) {
+          finish = true;
+          break;
+        }
+        if (__builtin_amdgcn_s_memrealtime() > deadline) {
+          uint32_t o2 = 0;
+          if (lane == 0) o2 = __hip_atomic_fetch_or(cnt, kAbandon, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          o2 = __builtin_amdgcn_readfirstlane(o2);
+          finish = (o2 & kArrivals) == (uint32_t)S;  // all arrived meanwhile: still ours
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+  } else {
+    // Last to arrive at a column its owner gave up on: finish it here.
+    finish = (old & kAbandon) != 0 && (old & kArrivals) == (uint32_t)(S - 1);
+  }
+  if (!finish) {
+    write_stamps();
+    return;
+  }
+  if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // Rank-order sum (this rank's partial from registers), one bf16 store per
+  // quad. BATCH quads at a time keep BATCH * (S - 1) loads in flight.
+  constexpr int PAIRS = RG * NT;
+  auto reduce = [&]<int BATCH, int OTHERS>() {
+#pragma unroll
+    for (int p0 = 0; p0 < PAIRS; p0 += BATCH) {
+      f32x4 v[BATCH][OTHERS];
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        if (p0 + b < PAIRS) {
+          const int rg = (p0 + b) / NT, tt = (p0 + b) % NT;
+#pragma unroll
+          for (int r = 0; r < OTHERS; ++r) {
+            const int rr = r < rank ? r : r + 1;  // the other ranks, in order
+            v[b][r] = __builtin_bit_cast(f32x4, ld16_coherent_if(in_t(tt), pr, p_off(rr, rg, tt)));
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        if (p0 + b < PAIRS) {
+          const int rg = (p0 + b) / NT, tt = (p0 + b) % NT;
+          const f32x4 mine = acc[rg][tt];
+          // Rank r's partial: this wave's own for r == rank, else the loaded
+          // one at index r (below rank) or r - 1 (above).
+          auto part_of = [&](int r) -> f32x4 {
+            const f32x4 below = v[b][r < OTHERS ? r : OTHERS - 1];
+            const f32x4 above = v[b][r > 0 ? r - 1 : 0];
+            return r == rank ? mine : (r < rank ? below : above);
+          };
+          f32x4 tot = part_of(0);
+#pragma unroll
+          for (int r = 1; r <= OTHERS; ++r) tot += part_of(r);
+          st8_if(in_t(tt), bf16_quad(tot), cr, c_off(rg, tt));
+        }
+      }
+    }
+  };
+  if (S == 2) {
+    reduce.template operator()<PAIRS, 1>();
+  } else if (S == 4) {
+    reduce.template operator()<(PAIRS < 8 ? PAIRS : 8), 3>();
+  } else {
+    reduce.template operator()<(NT >= 7 ? 2 : 4), 7>();
+  }
+  write_stamps();
+}
+
+// ---- configurations -------------------------------------------------------
+
+namespace {
+
+template <int NT, bool MX>
+hipError_t launch_wide_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((splitk_wide_kernel<NT, MX>), dim3(t.grid), dim3(t.threads), t.lds, s, p);
+  return hipGetLastError();
+}
+
+template <bool MX>
+hipError_t launch_wide_fmt(const Tactic& t, const GemmParams& p, hipStream_t s) {
+  switch (t.nt) {
+    case 3: return launch_wide_one<3, MX>(t, p, s);
+    case 4: return launch_wide_one<4, MX>(t, p, s);
+    case 5: return launch_wide_one<5, MX>(t, p, s);
+    case 6: return launch_wide_one<6, MX>(t, p, s);
+    case 7: return launch_wide_one<7, MX>(t, p, s);
+    case 8: return launch_wide_one<8, MX>(t, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool wide_fits(int T, int N, int ks, int S, bool mx, Tactic* t) {
+  const int nt = (T + 15) / 16;
+  if (nt < 3 || nt > 8 || N % kWideRows || ks <= 0) return false;
+  const int kc = wide_kc(nt);
+  if (ks % kc) return false;
+  (void)mx;
+  t->kind = 3;
+  t->nt = nt;
+  t->rg = 2;
+  t->wk = 1;
+  t->wn = kWideWaves;
+  t->d = mx ? (nt <= 4 ? 4 : 2) : 8;
+  t->c = 1;
+  t->kc = kc;
+  t->tile_n = kWideRows;
+  t->threads = 64 * kWideWaves;
+  t->lds = 2 * 16 * nt * kc * 2;
+  t->grid = (N / kWideRows) * S;
+  t->shape = 0;
+  t->fold = 1;
+  (void)S;
+  return true;
+}
+
+hipError_t launch_wide(const Tactic& t, const GemmParams& p, hipStream_t s) {
+  return t.mx ? launch_wide_fmt<true>(t, p, s) : launch_wide_fmt<false>(t, p, s);
+}
+
+}  // namespace skg

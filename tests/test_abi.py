@@ -101,6 +101,9 @@ def test_tactics_cover_the_workloads(T, N, K, S, mx):
     assert N % t["tile_n"] == 0
     if t["kind"] == "tiled":
         assert t["grid"] == (N // t["tile_n"]) * S
+    elif t["kind"] == "wide":  # 256-row tiles, one per workgroup per split rank, X in chunks
+        assert t["tile_n"] == 256 and t["grid"] == (N // 256) * S and 33 <= min(T, 128)
+        assert (K // S) % t["kc"] == 0 and t["lds"] == 2 * 16 * t["nt"] * t["kc"] * 2
     elif t["kind"] == "cluster":  # one workgroup per tile of 16/fold rows, S rank groups of waves
         assert t["tile_n"] * t["fold"] == 16 and t["grid"] == N // t["tile_n"]
         assert t["threads"] % (64 * S) == 0 and t["threads"] <= 1024

@@ -345,6 +345,49 @@ def test_owner_handover(wait, shape, monkeypatch):
             assert_parity(run_bf16(x, None, S, W=W), ref, K, f"hand-over T={T} S={S} rep {rep}")
 
 
+WIDE_CASES = [(40, 512, 4096, 4), (100, 256, 2048, 2), (128, 768, 1024, 1), (64, 512, 8192, 8),
+              (33, 256, 512, 1), (77, 512, 2048, 4)]
+WIDE_MX_CASES = [(48, 256, 2048, 2), (120, 512, 4096, 8), (65, 256, 1024, 1)]
+
+
+@pytest.mark.parametrize("wait", [None, "0"])
+def test_wide_kernel(wait, monkeypatch):
+    """The wide-tile kernel (33..128 tokens): every token-tile count it is
+    built for, ragged T, every split, bf16 and MXFP4; with the owner wait at
+    0 the columns go to the last rank to arrive instead."""
+    monkeypatch.setenv("SKGEMM_KIND", "3")
+    if wait is not None:
+        monkeypatch.setenv("SKGEMM_OWNER_WAIT", wait)
+    for (T, N, K, S) in WIDE_CASES:
+        tac = sk.skgemm_tactic_for(T, N, K, S)
+        log(f"wide wait={wait}: bf16 T={T} N={N} K={K} S={S} tactic={tac}")
+        assert tac["kind"] == "wide"
+        x, w = workloads.small_bf16_case(T, K, N, seed=9000 + T + S)
+        ref = G.gemm_bf16_ref(x, w)
+        W = to_dev_bf16(w)
+        for rep in range(2):
+            assert_parity(run_bf16(x, None, S, W=W), ref, K, f"wide T={T} S={S} rep {rep}")
+    for (T, N, K, S) in WIDE_MX_CASES:
+        tac = sk.skgemm_tactic_for(T, N, K, S, True)
+        log(f"wide wait={wait}: mxfp4 T={T} N={N} K={K} S={S} tactic={tac}")
+        assert tac["kind"] == "wide"
+        x, wq, ws = workloads.small_mxfp4_case(T, K, N, seed=9100 + T + S)
+        assert_parity(run_mxfp4(x, wq, ws, S), G.gemm_mxfp4_ref(x, wq, ws), K, f"wide mx T={T} S={S}")
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 8])
+def test_wide_integer_exact(S, monkeypatch):
+    monkeypatch.setenv("SKGEMM_KIND", "3")
+    for T in (33, 64, 97, 128):
+        N, K = 512, 4096
+        log(f"wide integer exact T={T} S={S} tactic={sk.skgemm_tactic_for(T, N, K, S)}")
+        x, w = workloads.integer_bf16_case(T, K, N, seed=9200 + T + S, mag=2)
+        exact = G.gemm_bf16_ref(x, w)
+        assert np.max(np.abs(exact)) < 2**24
+        want = F.f32_to_bf16_rne(exact.astype(np.float32))
+        assert np.array_equal(F.bf16_bits_to_f64(run_bf16(x, w, S)), F.bf16_bits_to_f64(want))
+
+
 def test_timeline_stamps(monkeypatch):
     """Opt-in phase stamps: five non-decreasing device-clock values per
     workgroup, results unchanged, and nothing written once turned off."""

@@ -39,7 +39,7 @@ SEED_BASE = 20260
 SWEEP_T = (1, 2, 4, 8, 16, 24, 32, 64, 128)
 # split_k per T for the K = N = 16384 sweep (a tuning choice, not part of the
 # method: every choice in {1, 2, 4, 8} gives results within the same bound).
-SWEEP_SPLIT = {1: 8, 2: 8, 4: 8, 8: 8, 16: 8, 24: 8, 32: 8, 64: 2, 128: 2}
+SWEEP_SPLIT = {1: 8, 2: 8, 4: 8, 8: 8, 16: 8, 24: 8, 32: 8, 64: 4, 128: 4}
 
 
 @dataclass(frozen=True)
