@@ -107,21 +107,32 @@ class Case:
         else:
             sk.skgemm_bf16(w[0], self.X, self.C, wl.T, wl.N, wl.K, wl.split_k, stream)
 
-    def time(self, steps: int, warmup: int, rotate: bool = True) -> dict:
+    def time(self, steps: int, warmup: int, rotate: bool = True, probe: bool = False) -> dict:
+        """Per-launch time of exactly `steps` launches replayed from one graph.
+        probe=True times the streaming-read reference over the same rotated
+        weight buffers instead of the GEMM."""
         torch = self.torch
         import split_reduction_amd as sk
 
         wl = self.wl
         stream = torch.cuda.Stream()
         sk.skgemm_reserve(wl.T, wl.N, wl.split_k, stream)
+        if probe:
+            sink = torch.zeros(512, dtype=torch.int32, device="cuda:0")
+
+            def launch(i, st):
+                w = self.weights[i % len(self.weights)][0]
+                sk.skgemm_read_probe(w, w.numel() * w.element_size(), sink, st)
+        else:
+            launch = self.launch
         with torch.cuda.stream(stream):
             for i in range(warmup):
-                self.launch(i if rotate else 0, stream)
+                launch(i if rotate else 0, stream)
         stream.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for i in range(steps):
-                self.launch(i if rotate else 0, stream)
+                launch(i if rotate else 0, stream)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             g.replay()  # the graph's own first replay (uploads it); untimed
@@ -156,6 +167,9 @@ def run_workload(wl, steps, warmup, host_w=None) -> dict:
     case = Case(wl, host_w)
     cold = case.time(steps, warmup, rotate=True)
     hot = case.time(steps, warmup, rotate=False)
+    probe = case.time(steps, warmup, rotate=True, probe=True)
+    probe_bytes = case.weights[0][0].numel() * case.weights[0][0].element_size()
+    probe_tbps = probe_bytes / (probe["t_us"] * 1e-6) / 1e12
     tac = sk.skgemm_tactic_for(wl.T, wl.N, wl.K, wl.split_k, wl.kind == "mxfp4")
     out = {
         "workload": wl.name, "kind": wl.kind, "T": wl.T, "K": wl.K, "N": wl.N,
@@ -168,6 +182,11 @@ def run_workload(wl, steps, warmup, host_w=None) -> dict:
         "frac_mfma_peak": round(cold["TFLOPs"] / BF16_MFMA_PEAK_TFLOPS, 5),
         "hot_t_us": round(hot["t_us"], 3),
         "hot_weight_TBps": round(hot["weight_TBps"], 4),
+        # The streaming-read reference over the same rotated buffers: what a
+        # plain coalesced read of this many bytes reaches on this GPU.
+        "read_probe": {"bytes": probe_bytes, "t_us": round(probe["t_us"], 3),
+                       "TBps": round(probe_tbps, 4),
+                       "gemm_frac": round(cold["weight_TBps"] / probe_tbps, 4)},
         "tactic": {k: tac[k] for k in ("nt", "rg", "wk", "wn", "d", "kc", "tile_n", "grid")},
         "_algo_bytes": case.algo_bytes(),
     }
@@ -465,6 +484,7 @@ def main() -> None:
         },
         "cpu_baseline": cpu,
         "hot_cache": {"t_us": h["hot_t_us"], "weight_TBps": h["hot_weight_TBps"]},
+        "read_probe": h["read_probe"],
         "tactic": h["tactic"],
         "workloads": [{k: v for k, v in r.items() if not k.startswith("_")} for r in extra],
         "kernel_source_sha": kernel_source_hash(),

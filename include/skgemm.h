@@ -145,6 +145,18 @@ SKGEMM_API int skgemm_pack_e4m3(const float* in, uint32_t* out, size_t n_quads, 
 SKGEMM_API int skgemm_wave_sum(const float* in, float* out, size_t n_waves, hipStream_t stream);
 
 /*
+ * skgemm_read_probe: a reference for the weight stream, not part of the
+ * method: reads `bytes` of device memory at src once, with plain coalesced
+ * 16-byte loads, 512 workgroups of 1024 lanes each reading one contiguous
+ * block, and computes nothing from them. The time it takes is the
+ * streaming-read rate the GEMM kernels are compared with at the same byte
+ * count. src: 16-byte aligned, bytes a multiple of 16. sink: device memory for
+ * 512 uint32 words, which the probe does not normally write. Returns SKGEMM_EINVAL for a null pointer or a bad size,
+ * SKGEMM_EALIGN for misaligned pointers.
+ */
+SKGEMM_API int skgemm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+/*
  * skgemm_tactic_for: describe, as a short JSON object written to buf
  * (NUL-terminated, truncated to buf_len), the kernel configuration a call with
  * these sizes would launch. mxfp4 != 0 selects the MXFP4 entry point. Returns

@@ -49,6 +49,7 @@ def _declare(lib):
         "skgemm_tactic_for": [i, i, i, i, i, ctypes.c_char_p, sz],
         "skgemm_last_hip_error": [],
         "skgemm_set_timeline": [vp, sz],
+        "skgemm_read_probe": [vp, sz, vp, st],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -161,6 +162,11 @@ def skgemm_tactic_for(T: int, N: int, K: int, split_k: int, mxfp4: bool = False)
 def skgemm_set_timeline(buf, capacity: int) -> None:
     """Opt-in per-workgroup phase stamps of the stream kernel (None turns them off)."""
     _check(lib().skgemm_set_timeline(_ptr(buf), capacity if buf is not None else 0), "skgemm_set_timeline")
+
+
+def skgemm_read_probe(src, nbytes: int, sink, stream=None) -> None:
+    """Plain coalesced read of nbytes at src (the streaming-read reference)."""
+    _check(lib().skgemm_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "skgemm_read_probe")
 
 
 def skgemm_strerror(code: int) -> str:

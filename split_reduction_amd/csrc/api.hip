@@ -254,6 +254,14 @@ SKGEMM_API int skgemm_set_timeline(void* buf, size_t capacity) {
   return SKGEMM_OK;
 }
 
+SKGEMM_API int skgemm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (src == nullptr || sink == nullptr || bytes % 16 != 0) return SKGEMM_EINVAL;
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0 || reinterpret_cast<uintptr_t>(sink) % 4 != 0)
+    return SKGEMM_EALIGN;
+  const hipError_t e = skg::launch_read_probe(src, bytes, sink, stream);
+  return e == hipSuccess ? SKGEMM_OK : hip_fail(e);
+}
+
 SKGEMM_API const char* skgemm_strerror(int code) {
   switch (code) {
     case SKGEMM_OK: return "success";

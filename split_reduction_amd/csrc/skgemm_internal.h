@@ -74,5 +74,10 @@ hipError_t launch_pack_e4m3(const float* in, uint32_t* out, size_t n_quads, hipS
 hipError_t launch_wave_sum(const float* in, float* out, size_t n_waves, hipStream_t s);
 hipError_t launch_mxfp4_dequant(const void* wq, const void* ws, void* out, int N, int K,
                                 hipStream_t s);
+// Plain coalesced read of `bytes` (a multiple of 16) with kReadProbeBlocks
+// workgroups of 1024 lanes (two per CU); sink needs kReadProbeBlocks words.
+constexpr int kReadProbeBlocks = 512;
+constexpr uint32_t kReadProbeMagic = 0x9E3779B9u;
+hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace skg

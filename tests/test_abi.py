@@ -74,6 +74,10 @@ def test_argument_checks_before_any_device_work():
     assert lib.skgemm_pack_bf16(None, None, 0, None) == sk.SKGEMM_OK
     assert lib.skgemm_wave_sum(a, None, 1, None) == sk.SKGEMM_EINVAL
     assert lib.skgemm_mxfp4_dequant(a, a, a, 16, 48, None) == sk.SKGEMM_ESHAPE
+    # the streaming-read reference
+    assert lib.skgemm_read_probe(None, 64, a, None) == sk.SKGEMM_EINVAL
+    assert lib.skgemm_read_probe(a, 24, a, None) == sk.SKGEMM_EINVAL
+    assert lib.skgemm_read_probe(a + 8, 64, a, None) == sk.SKGEMM_EALIGN
 
 
 def test_strerror_covers_every_code():

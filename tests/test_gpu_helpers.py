@@ -108,3 +108,19 @@ def test_mxfp4_dequant_workload_tensor():
     sk.skgemm_mxfp4_dequant(to_dev_u8(wq), to_dev_u8(ws), out, w.N, w.K)
     t.cuda.synchronize()
     assert np.array_equal(bf16_bits(out), F.mxfp4_dequant_bf16_bits(wq, ws))
+
+
+def test_read_probe_reads_and_writes_nothing():
+    """The streaming-read reference runs over odd and large sizes and leaves
+    its sink untouched (it stores only on an impossible fold value)."""
+    t = torch()
+    buf = t.randint(0, 2**31 - 1, (1 << 22,), dtype=t.int32, device=DEV)
+    sink = t.zeros(512, dtype=t.int32, device=DEV)
+    for nbytes in (16, 4096 + 16, 1 << 20, buf.numel() * 4):
+        log(f"read probe {nbytes} bytes")
+        sk.skgemm_read_probe(buf, nbytes, sink)
+    t.cuda.synchronize()
+    assert int(sink.abs().sum().item()) == 0
+    with pytest.raises(sk.SkgemmError) as e:
+        sk.skgemm_read_probe(buf, 24, sink)
+    assert e.value.code == sk.SKGEMM_EINVAL
