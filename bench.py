@@ -53,16 +53,27 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 ROTATE_BYTES = 1 << 30
 HEADLINE = "bf16_t8_k7168_n2048"
-KERNEL_SOURCES = ["split_reduction_amd/csrc/gemm.hip", "split_reduction_amd/csrc/device/types.h",
-                  "split_reduction_amd/csrc/device/pack.h", "split_reduction_amd/csrc/device/mxfp4.h",
-                  "split_reduction_amd/csrc/device/mfma.h"]
+CSRC = os.path.join("split_reduction_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
+def kernel_sources() -> list:
+    """Every kernel, launch and header source of the library (repo-relative)."""
+    out = []
+    for d, _, files in os.walk(os.path.join(ROOT, CSRC)):
+        out += [os.path.relpath(os.path.join(d, f), ROOT) for f in files if f.endswith((".hip", ".h"))]
+    return sorted(out)
+
+
+def kernel_source_hash(read=None) -> str:
+    """Hash of the library sources; HBM counters are used only while it matches."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    for rel in kernel_sources():
+        if read is None:
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                data = f.read()
+        else:
+            data = read(rel)
+        h.update(rel.encode() + b"\0" + data)
     return h.hexdigest()[:16]
 
 
