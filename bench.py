@@ -166,16 +166,80 @@ class Case:
             "TFLOPs": wl.flops() / t_s / 1e12,
         }
 
+    def time_batched(self, L: int, steps: int, warmup: int) -> dict:
+        """Per-launch time of batched launches of L independent problems
+        (distinct weights and activations per problem), cold rotated weights."""
+        torch = self.torch
+        import split_reduction_amd as sk
+
+        wl = self.wl
+        dev = "cuda:0"
+        R = max(2, math.ceil(ROTATE_BYTES / (L * wl.weight_bytes())))
+        base = self.weights[0]
+        wq = torch.empty((R, L) + tuple(base[0].shape), dtype=base[0].dtype, device=dev)
+        wq.copy_(base[0].expand(R, L, *base[0].shape))
+        ws = None
+        if wl.kind == "mxfp4":
+            ws = torch.empty((R, L) + tuple(base[1].shape), dtype=base[1].dtype, device=dev)
+            ws.copy_(base[1].expand(R, L, *base[1].shape))
+        X = self.X.expand(L, *self.X.shape).contiguous()
+        C = torch.empty((L, wl.T, wl.N), dtype=torch.bfloat16, device=dev)
+        wstride = base[0].numel() * base[0].element_size()
+        xstride = self.X.numel() * 2
+        cstride = wl.T * wl.N * 2
+        stream = torch.cuda.Stream()
+        sk.skgemm_reserve_batched(wl.T, wl.N, wl.split_k, L, stream)
+
+        def launch(i, st):
+            r = i % R
+            if wl.kind == "mxfp4":
+                sk.skgemm_mxfp4_batched(wq[r], ws[r], X, C, wl.T, wl.N, wl.K, wl.split_k, L, wstride,
+                                        base[1].numel(), xstride, cstride, st)
+            else:
+                sk.skgemm_bf16_batched(wq[r], X, C, wl.T, wl.N, wl.K, wl.split_k, L, wstride, xstride,
+                                       cstride, st)
+
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                launch(i, stream)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(steps):
+                launch(i, stream)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            start.record(stream)
+            g.replay()
+            end.record(stream)
+        end.synchronize()
+        t_s = start.elapsed_time(end) * 1e-3 / steps
+        del g, wq, ws, X, C
+        return {"L": L, "t_us": round(t_s * 1e6, 3), "t_us_per_problem": round(t_s * 1e6 / L, 3),
+                "weight_TBps": round(L * wl.weight_bytes() / t_s / 1e12, 4)}
+
     def algo_bytes(self) -> int:
         """Compulsory bytes of one call: weights + X + C."""
         wl = self.wl
         return wl.weight_bytes() + 2 * wl.T * wl.K + 2 * wl.T * wl.N
 
 
+BATCH_L = 8  # problems per batched launch reported for the small workloads
+BATCH_MAX_WEIGHT_BYTES = 64 << 20
+
+
 def run_workload(wl, steps, warmup, host_w=None) -> dict:
     import split_reduction_amd as sk
 
     case = Case(wl, host_w)
+    batched = None
+    if wl.weight_bytes() <= BATCH_MAX_WEIGHT_BYTES:
+        batched = case.time_batched(BATCH_L, steps, warmup)
     cold = case.time(steps, warmup, rotate=True)
     hot = case.time(steps, warmup, rotate=False)
     probe = case.time(steps, warmup, rotate=True, probe=True)
@@ -201,6 +265,8 @@ def run_workload(wl, steps, warmup, host_w=None) -> dict:
         "tactic": {k: tac[k] for k in ("nt", "rg", "wk", "wn", "d", "kc", "tile_n", "grid")},
         "_algo_bytes": case.algo_bytes(),
     }
+    if batched is not None:
+        out["batched"] = batched
     del case
     import torch
 
@@ -496,6 +562,7 @@ def main() -> None:
         "cpu_baseline": cpu,
         "hot_cache": {"t_us": h["hot_t_us"], "weight_TBps": h["hot_weight_TBps"]},
         "read_probe": h["read_probe"],
+        "batched": h.get("batched"),
         "tactic": h["tactic"],
         "workloads": [{k: v for k, v in r.items() if not k.startswith("_")} for r in extra],
         "kernel_source_sha": kernel_source_hash(),

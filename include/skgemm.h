@@ -67,6 +67,7 @@ enum skgemm_status {
  * token counts above 128 are processed in blocks of 128 rows. */
 #define SKGEMM_MAX_N (1 << 18)
 #define SKGEMM_MAX_K (1 << 22)
+#define SKGEMM_MAX_BATCH 4096
 
 /*
  * skgemm_bf16: C = X . W^T with bf16 W, X, C and FP32 accumulation.
@@ -96,6 +97,29 @@ SKGEMM_API int skgemm_mxfp4(const void* Wq, const void* Wscale, const void* X, v
                             int N, int K, int split_k, hipStream_t stream);
 
 /*
+ * skgemm_bf16_batched, skgemm_mxfp4_batched: L independent problems of one
+ * shape in one launch (the pages' batch dimension L: SplitKGemm.kernel takes
+ * A (M,K,L), B (N,K,L), C (M,N,L) and SplitKGemm.__call__ launches the L
+ * problems as the third grid dimension). Problem l reads W + l*w_stride, X + l*x_stride (and Wscale +
+ * l*wscale_stride) and writes C + l*c_stride; strides are in bytes. Each
+ * problem is computed exactly as the single call with the same arguments
+ * would compute it, and one launch amortises the dispatch cost over L.
+ *   1 <= L <= SKGEMM_MAX_BATCH. For L > 1: w/wq, x and c strides are
+ *   multiples of 16 (every problem's operands stay 16-byte aligned); a zero
+ *   W or X stride shares that operand across the batch; c_stride >= T*N*2 so
+ *   outputs do not overlap (SKGEMM_EINVAL otherwise; SKGEMM_EALIGN for a
+ *   misaligned stride). Other arguments as skgemm_bf16 / skgemm_mxfp4; with
+ *   split_k > 1 the workspace holds L problems (skgemm_reserve_batched).
+ */
+SKGEMM_API int skgemm_bf16_batched(const void* W, const void* X, void* C, int T, int N, int K,
+                                   int split_k, int L, size_t w_stride, size_t x_stride,
+                                   size_t c_stride, hipStream_t stream);
+SKGEMM_API int skgemm_mxfp4_batched(const void* Wq, const void* Wscale, const void* X, void* C,
+                                    int T, int N, int K, int split_k, int L, size_t wq_stride,
+                                    size_t wscale_stride, size_t x_stride, size_t c_stride,
+                                    hipStream_t stream);
+
+/*
  * skgemm_reserve: make sure the workspace of (current device, stream) can
  * serve any call with T <= max_T (capped at 128, the block size), N <= max_N
  * and split_k <= max_split_k. Call it before capturing a stream into a HIP
@@ -105,6 +129,13 @@ SKGEMM_API int skgemm_mxfp4(const void* Wq, const void* Wscale, const void* X, v
  * May synchronise `stream` when it replaces a smaller workspace.
  */
 SKGEMM_API int skgemm_reserve(int max_T, int max_N, int max_split_k, hipStream_t stream);
+
+/*
+ * skgemm_reserve_batched: skgemm_reserve for batched calls of up to max_L
+ * problems (1 <= max_L <= SKGEMM_MAX_BATCH); skgemm_reserve is max_L = 1.
+ */
+SKGEMM_API int skgemm_reserve_batched(int max_T, int max_N, int max_split_k, int max_L,
+                                      hipStream_t stream);
 
 /* skgemm_release: free every workspace of the calling process. Synchronises
  * the device first. Not to be called while other threads enqueue work. */

@@ -41,6 +41,9 @@ def _declare(lib):
         "skgemm_bf16": [vp, vp, vp, i, i, i, i, st],
         "skgemm_mxfp4": [vp, vp, vp, vp, i, i, i, i, st],
         "skgemm_reserve": [i, i, i, st],
+        "skgemm_reserve_batched": [i, i, i, i, st],
+        "skgemm_bf16_batched": [vp, vp, vp, i, i, i, i, i, sz, sz, sz, st],
+        "skgemm_mxfp4_batched": [vp, vp, vp, vp, i, i, i, i, i, sz, sz, sz, sz, st],
         "skgemm_release": [],
         "skgemm_mxfp4_dequant": [vp, vp, vp, i, i, st],
         "skgemm_pack_bf16": [vp, vp, sz, st],
@@ -124,6 +127,27 @@ def skgemm_mxfp4(Wq, Wscale, X, C, T: int, N: int, K: int, split_k: int, stream=
     code = lib().skgemm_mxfp4(_ptr(Wq), _ptr(Wscale), _ptr(X), _ptr(C), T, N, K, split_k,
                               _stream(stream))
     _check(code, "skgemm_mxfp4")
+
+
+def skgemm_bf16_batched(W, X, C, T: int, N: int, K: int, split_k: int, L: int, w_stride: int,
+                        x_stride: int, c_stride: int, stream=None) -> None:
+    """L problems of one shape in one launch; strides in bytes."""
+    code = lib().skgemm_bf16_batched(_ptr(W), _ptr(X), _ptr(C), T, N, K, split_k, L, w_stride, x_stride,
+                                     c_stride, _stream(stream))
+    _check(code, "skgemm_bf16_batched")
+
+
+def skgemm_mxfp4_batched(Wq, Wscale, X, C, T: int, N: int, K: int, split_k: int, L: int, wq_stride: int,
+                         wscale_stride: int, x_stride: int, c_stride: int, stream=None) -> None:
+    """L MXFP4 problems of one shape in one launch; strides in bytes."""
+    code = lib().skgemm_mxfp4_batched(_ptr(Wq), _ptr(Wscale), _ptr(X), _ptr(C), T, N, K, split_k, L,
+                                      wq_stride, wscale_stride, x_stride, c_stride, _stream(stream))
+    _check(code, "skgemm_mxfp4_batched")
+
+
+def skgemm_reserve_batched(max_T: int, max_N: int, max_split_k: int, max_L: int, stream=None) -> None:
+    _check(lib().skgemm_reserve_batched(max_T, max_N, max_split_k, max_L, _stream(stream)),
+           "skgemm_reserve_batched")
 
 
 def skgemm_reserve(max_T: int, max_N: int, max_split_k: int, stream=None) -> None:

@@ -119,20 +119,55 @@ size_t part_bytes_for(int T, int N, int S) {
 }
 size_t counters_for(int N) { return (size_t)N / 16; }
 
+// Compute units of the current device (the owner wait is used only while the
+// whole grid fits on them).
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  cache[dev] = n;
+  return n;
+}
+
+// A batch of L problems of one shape; strides in bytes (problem l of W at
+// w + l * bw, and so on).
+struct Batch {
+  int L = 1;
+  uint64_t bw = 0, bws = 0, bx = 0, bc = 0;
+};
+
+int check_batch(const Batch& b, int T, int N) {
+  if (b.L < 1 || b.L > SKGEMM_MAX_BATCH) return SKGEMM_EINVAL;
+  if (b.L == 1) return SKGEMM_OK;
+  if ((b.bw | b.bx | b.bc) % 16 != 0) return SKGEMM_EALIGN;  // Wscale needs no alignment
+  if (b.bc < (uint64_t)T * (uint64_t)N * 2) return SKGEMM_EINVAL;  // outputs must not overlap
+  return SKGEMM_OK;
+}
+
 int run_gemm(bool mx, const void* w, const void* ws, const void* x, void* c, int T, int N, int K,
-             int S, hipStream_t stream) {
+             int S, hipStream_t stream, const Batch& batch = Batch{}) {
   int rc = check_gemm(mx, w, ws, x, c, T, N, K, S, true);
   if (rc != SKGEMM_OK) return rc;
+  rc = check_batch(batch, T, N);
+  if (rc != SKGEMM_OK) return rc;
   if (T == 0 || N == 0) return SKGEMM_OK;
+  const int L = batch.L;
   Workspace wsp;
   if (S > 1) {
-    rc = ensure_workspace(stream, part_bytes_for(T, N, S), counters_for(N), &wsp);
+    rc = ensure_workspace(stream, part_bytes_for(T, N, S) * (size_t)L, counters_for(N) * (size_t)L, &wsp);
     if (rc != SKGEMM_OK) return rc;
   }
+  const int cus = device_cus();
   for (int t0 = 0; t0 < T; t0 += kTokenBlock) {
     const int tb = std::min(kTokenBlock, T - t0);
-    skg::Tactic tac;
-    if (!skg::pick_tactic(tb, N, K, S, mx, &tac)) return SKGEMM_ESHAPE;
+    skg::Tactic tac{};
+    if (!skg::pick_tactic(tb, N, K, S, mx, &tac, L)) return SKGEMM_ESHAPE;
     skg::GemmParams p{};
     p.w = w;
     p.wscale = static_cast<const uint8_t*>(ws);
@@ -148,7 +183,18 @@ int run_gemm(bool mx, const void* w, const void* ws, const void* x, void* c, int
     p.kc = tac.kc;
     p.nchunks = (tac.kc > 0) ? p.ks / tac.kc : 0;
     p.stamps = ((size_t)tac.grid * 8 <= g_stamps_cap.load()) ? g_stamps.load() : nullptr;
-    p.owner_wait = owner_wait_ticks();
+    // Owners wait for their peers only while every workgroup of the launch can
+    // be resident at once; beyond, they hand their tiles over at once.
+    const bool all_resident =
+        tac.resident > 0 && cus > 0 && (long)tac.grid * L <= (long)cus * tac.resident;
+    p.owner_wait = all_resident ? owner_wait_ticks() : 0u;
+    p.L = L;
+    p.bw = batch.bw;
+    p.bws = batch.bws;
+    p.bx = batch.bx;
+    p.bc = batch.bc;
+    p.bpart = (uint64_t)S * (uint64_t)tb * (uint64_t)N;
+    p.bcnt = (uint32_t)counters_for(N);
     hipError_t e = skg::launch_gemm(tac, p, stream);
     if (e != hipSuccess) return hip_fail(e);
   }
@@ -169,12 +215,42 @@ SKGEMM_API int skgemm_mxfp4(const void* Wq, const void* Wscale, const void* X, v
   return run_gemm(true, Wq, Wscale, X, C, T, N, K, split_k, stream);
 }
 
+SKGEMM_API int skgemm_bf16_batched(const void* W, const void* X, void* C, int T, int N, int K,
+                                   int split_k, int L, size_t w_stride, size_t x_stride,
+                                   size_t c_stride, hipStream_t stream) {
+  Batch b;
+  b.L = L;
+  b.bw = w_stride;
+  b.bx = x_stride;
+  b.bc = c_stride;
+  return run_gemm(false, W, nullptr, X, C, T, N, K, split_k, stream, b);
+}
+
+SKGEMM_API int skgemm_mxfp4_batched(const void* Wq, const void* Wscale, const void* X, void* C,
+                                    int T, int N, int K, int split_k, int L, size_t wq_stride,
+                                    size_t wscale_stride, size_t x_stride, size_t c_stride,
+                                    hipStream_t stream) {
+  Batch b;
+  b.L = L;
+  b.bw = wq_stride;
+  b.bws = wscale_stride;
+  b.bx = x_stride;
+  b.bc = c_stride;
+  return run_gemm(true, Wq, Wscale, X, C, T, N, K, split_k, stream, b);
+}
+
 SKGEMM_API int skgemm_reserve(int max_T, int max_N, int max_split_k, hipStream_t stream) {
+  return skgemm_reserve_batched(max_T, max_N, max_split_k, 1, stream);
+}
+
+SKGEMM_API int skgemm_reserve_batched(int max_T, int max_N, int max_split_k, int max_L,
+                                      hipStream_t stream) {
   if (max_T < 0 || max_N < 0 || max_split_k < 1 || max_split_k > 8) return SKGEMM_EINVAL;
+  if (max_L < 1 || max_L > SKGEMM_MAX_BATCH) return SKGEMM_EINVAL;
   if (max_N > SKGEMM_MAX_N) return SKGEMM_ESHAPE;
   Workspace w;
-  return ensure_workspace(stream, part_bytes_for(max_T, max_N, max_split_k), counters_for(max_N),
-                          &w);
+  return ensure_workspace(stream, part_bytes_for(max_T, max_N, max_split_k) * (size_t)max_L,
+                          counters_for(max_N) * (size_t)max_L, &w);
 }
 
 SKGEMM_API int skgemm_release(void) {

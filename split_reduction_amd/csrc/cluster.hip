@@ -54,6 +54,7 @@ constexpr int cluster_depth(int nt, int c, bool mx) {
 // b*R .. b*R + R - 1 over all of K.
 template <int NT, int F, int WT, int C, bool MX>
 __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
+  select_problem(p);
   constexpr int R = 16 / F;                    // weight rows of the tile
   constexpr int TF = 16 / F;                   // token slots of one fold
   constexpr int LOADS = MX ? 1 : C;            // 16-byte weight loads per lane per step
@@ -245,7 +246,7 @@ namespace {
 
 template <int NT, int F, int WT, int C, bool MX>
 hipError_t launch_cluster_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((splitk_cluster_kernel<NT, F, WT, C, MX>), dim3(t.grid), dim3(t.threads), 0, s, p);
+  hipLaunchKernelGGL((splitk_cluster_kernel<NT, F, WT, C, MX>), dim3(t.grid, p.L), dim3(t.threads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -68,6 +68,7 @@ __device__ __forceinline__ void lds_write16(uint8_t* smem, int slot, u32x4 v) {
 
 template <int NT, int RG, int WK, int WN, int D, int C, bool MX>
 __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p) {
+  select_problem(p);
   constexpr int THREADS = 64 * WK * WN;
   constexpr int TILE_N = 16 * RG * WN;
   constexpr int LOADS = MX ? 1 : C;          // 16-byte weight loads per row group per step
@@ -364,6 +365,7 @@ template <int NT, int WK, int WN, int D, int C, bool EPI, bool MX>
 __global__ __launch_bounds__(64 * WK * WN)
 __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu(NT, WK * WN))))
 void splitk_stream_kernel(GemmParams p) {
+  select_problem(p);
   constexpr int THREADS = 64 * WK * WN;
   constexpr int LOADS = MX ? 1 : C;
   constexpr int SUBS = MX ? 4 : C;
@@ -848,7 +850,7 @@ hipError_t launch_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
     return hipErrorInvalidValue;  // not built: pick_tactic never selects it
   } else {
     auto kern = splitk_gemm_kernel<NT, sh.rg, sh.wk, sh.wn, sh.d, sh.c, MX>;
-    hipLaunchKernelGGL(kern, dim3(t.grid), dim3(t.threads), t.lds, s, p);
+    hipLaunchKernelGGL(kern, dim3(t.grid, p.L), dim3(t.threads), t.lds, s, p);
     return hipGetLastError();
   }
 }
@@ -952,12 +954,13 @@ constexpr int kNumStreamShapes = sizeof(kStreamShapes) / sizeof(kStreamShapes[0]
 constexpr int kStreamMaxNT = 2;
 constexpr int kStreamMaxX = 128 * 1024;
 constexpr int kClusterMaxGrid = 512;
+constexpr long kClusterMaxBatchGrid = 8192;
 
 template <int NT, int SH, bool MX>
 hipError_t launch_stream_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
   constexpr StreamShape sh = kStreamShapes[SH];
   auto kern = splitk_stream_kernel<NT, sh.wk, sh.wn, sh.d, sh.c, sh.epi != 0, MX>;
-  hipLaunchKernelGGL(kern, dim3(t.grid), dim3(t.threads), t.lds, s, p);
+  hipLaunchKernelGGL(kern, dim3(t.grid, p.L), dim3(t.threads), t.lds, s, p);
   return hipGetLastError();
 }
 
@@ -989,7 +992,7 @@ int env_int(const char* name, int dflt) {
 }
 
 // Fills the geometry of persistent shape `si`; false if it does not apply.
-bool stream_fits(int si, int T, int N, int ks, int S, bool mx, Tactic* t) {
+bool stream_fits(int si, int T, int N, int ks, int S, bool mx, Tactic* t, int L = 1) {
   const StreamShape& c = kStreamShapes[si];
   if (t->nt > kStreamMaxNT || ks == 0) return false;
   const int step = mx ? 128 : 32 * c.c;
@@ -1011,7 +1014,7 @@ bool stream_fits(int si, int T, int N, int ks, int S, bool mx, Tactic* t) {
   if (per_cu > stream_wgs_per_cu(t->nt)) per_cu = stream_wgs_per_cu(t->nt);
   per_cu = env_int("SKGEMM_WG_PER_CU", per_cu);
   if (per_cu < 1) per_cu = 1;
-  long g = (256L * per_cu) / S;
+  long g = (256L * per_cu) / ((long)S * (L > 0 ? L : 1));  // the whole batch resident
   const long g_max = (n_tiles + c.wn - 1) / c.wn;  // every column gets a tile
   if (g > g_max) g = g_max;
   if (g < 1) g = 1;
@@ -1027,10 +1030,11 @@ bool stream_fits(int si, int T, int N, int ks, int S, bool mx, Tactic* t) {
   t->lds = (int)lds;
   t->grid = (int)g * S;
   t->shape = si;
+  t->resident = per_cu;
   return true;
 }
 
-bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
+bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L) {
   Tactic t{};
   t.nt = (T + 15) / 16;
   if (t.nt < 1) t.nt = 1;
@@ -1048,8 +1052,15 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
     if (cluster_fits(tr, N, ks, S, mx, env_int("SKGEMM_FOLD", 8), env_int("SKGEMM_CLUSTER_C", 0), &c)) {
       // Whole tiles per workgroup pay off while the grid is about one
       // workgroup per CU; beyond, the persistent kernel's staged activations
-      // and amortised ramp-up win.
-      if (kind == 2 || c.grid <= kClusterMaxGrid) {
+      // and amortised ramp-up win. Every cluster workgroup re-reads all of X
+      // from L2, T*2 bytes per tile row against the row's weight bytes; in a
+      // batch the cluster kernel stays only while that is small (measured:
+      // T=1 K=1024 N=1024 batches run 1.1 vs 1.6 us a problem on it, the
+      // T=8 K=7168 N=2048 ones 9.6 vs 6.4 us on the persistent kernel).
+      const double x_per_w = (double)tr * 2.0 / ((double)c.tile_n * (mx ? 0.53125 : 2.0));
+      const bool small = L == 1 ? c.grid <= kClusterMaxGrid
+                                : (x_per_w <= 0.5 && (long)c.grid * L <= kClusterMaxBatchGrid);
+      if (kind == 2 || small) {
         *out = c;
         return true;
       }
@@ -1060,7 +1071,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
   // SKGEMM_STREAM=<index> forces one of its shapes, for tuning runs).
   if (kind == 1 || kind < 0) {
     const int forced = env_int("SKGEMM_STREAM", -2);
-    if (forced >= 0 && forced < kNumStreamShapes && stream_fits(forced, tr, N, ks, S, mx, &t)) {
+    if (forced >= 0 && forced < kNumStreamShapes && stream_fits(forced, tr, N, ks, S, mx, &t, L)) {
       *out = t;
       return true;
     }
@@ -1076,7 +1087,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
       const int* pref = many;
       for (int si : many) {
         Tactic probe = t;
-        if (stream_fits(si, tr, N, ks, S, mx, &probe)) {
+        if (stream_fits(si, tr, N, ks, S, mx, &probe, L)) {
           const int groups = probe.grid / S;
           const int per_wg = (N / 16 + groups - 1) / groups;
           if (per_wg <= 4) pref = few;
@@ -1085,7 +1096,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out) {
       }
       for (int oi = 0; oi < kNumStreamShapes; ++oi) {
         const int si = pref[oi];
-        if (stream_fits(si, tr, N, ks, S, mx, &t)) {
+        if (stream_fits(si, tr, N, ks, S, mx, &t, L)) {
           *out = t;
           return true;
         }

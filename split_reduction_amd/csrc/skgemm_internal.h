@@ -19,10 +19,29 @@ struct GemmParams {
   int kc;       // K elements of X staged in LDS at a time; divides ks
   int nchunks;  // ks / kc
   uint64_t* stamps;  // optional per-workgroup phase stamps
-  uint32_t owner_wait;  // stream kernel: device-clock ticks (100 MHz) a tile's
-                        // owner waits for the other ranks before handing the
-                        // tile to the last to arrive
+  uint32_t owner_wait;  // device-clock ticks (100 MHz) a tile's owner waits for
+                        // the other ranks before handing the tile to the last
+                        // to arrive (0: hand over at once)
+  // A batch of independent problems of one shape (grid.y = L): problem l
+  // reads and writes at these strides from the pointers above.
+  int L;
+  uint64_t bw, bws, bx, bc;  // bytes between problems: W (or Wq), Wscale, X, C
+  uint64_t bpart;            // floats between problems' partials
+  uint32_t bcnt;             // counters between problems' counters
 };
+
+// Moves p's pointers to the problem of this workgroup (blockIdx.y).
+__device__ __forceinline__ void select_problem(GemmParams& p) {
+  const uint64_t l = blockIdx.y;
+  if (l == 0) return;
+  p.w = static_cast<const uint8_t*>(p.w) + l * p.bw;
+  p.wscale = p.wscale + l * p.bws;
+  p.x = static_cast<const uint8_t*>(p.x) + l * p.bx;
+  p.c = static_cast<uint8_t*>(p.c) + l * p.bc;
+  p.part = p.part + l * p.bpart;
+  p.cnt = p.cnt + l * (uint64_t)p.bcnt;
+  p.stamps = nullptr;  // stamps describe problem 0 only
+}
 
 // A kernel configuration. One workgroup computes a TILE_N x T tile over one K
 // slice; its WK * WN waves split that slice WK ways along K (interleaved load
@@ -47,11 +66,12 @@ struct Tactic {
                 // 3: wide tiles with double-buffered X chunks (33..128 tokens)
   int shape;    // index into the kind's shape table
   int fold;     // kind 2: K windows folded into one MFMA operand (tile rows 16/fold)
+  int resident; // workgroups per CU the grid sizing counts on (0: none assumed)
 };
 
 // Picks the configuration for a launch over T <= 128 rows; returns false if no
 // instantiated configuration fits (never for validated shapes).
-bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out);
+bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L = 1);
 
 // Fills the configuration of the one-workgroup-per-tile kernel (kind 2) for a
 // launch over T <= 32 rows, folding at most max_fold ways (force_c > 0 pins

@@ -43,6 +43,7 @@ constexpr int wide_kc(int nt) { return nt <= 4 ? 512 : 256; }  // K elements per
 
 template <int NT, bool MX>
 __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams p) {
+  select_problem(p);
   constexpr int RG = 2;                       // 16-row groups per wave
   constexpr int THREADS = 64 * kWideWaves;
   constexpr int SUBS = MX ? 4 : 1;            // MFMA K-steps per load step
@@ -337,7 +338,7 @@ namespace {
 
 template <int NT, bool MX>
 hipError_t launch_wide_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((splitk_wide_kernel<NT, MX>), dim3(t.grid), dim3(t.threads), t.lds, s, p);
+  hipLaunchKernelGGL((splitk_wide_kernel<NT, MX>), dim3(t.grid, p.L), dim3(t.threads), t.lds, s, p);
   return hipGetLastError();
 }
 
@@ -376,6 +377,7 @@ bool wide_fits(int T, int N, int ks, int S, bool mx, Tactic* t) {
   t->grid = (N / kWideRows) * S;
   t->shape = 0;
   t->fold = 1;
+  t->resident = 1;  // 128 KiB of X chunks (or ~200 registers a lane) per workgroup
   (void)S;
   return true;
 }

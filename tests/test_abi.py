@@ -74,6 +74,13 @@ def test_argument_checks_before_any_device_work():
     assert lib.skgemm_pack_bf16(None, None, 0, None) == sk.SKGEMM_OK
     assert lib.skgemm_wave_sum(a, None, 1, None) == sk.SKGEMM_EINVAL
     assert lib.skgemm_mxfp4_dequant(a, a, a, 16, 48, None) == sk.SKGEMM_ESHAPE
+    # batched calls: L range, stride alignment, overlapping outputs
+    assert lib.skgemm_bf16_batched(a, a, a, 2, 16, 64, 1, 0, 0, 0, 64, None) == sk.SKGEMM_EINVAL
+    assert lib.skgemm_bf16_batched(a, a, a, 2, 16, 64, 1, 5000, 0, 0, 64, None) == sk.SKGEMM_EINVAL
+    assert lib.skgemm_bf16_batched(a, a, a, 2, 16, 64, 1, 2, 8, 0, 64, None) == sk.SKGEMM_EALIGN
+    assert lib.skgemm_bf16_batched(a, a, a, 2, 16, 64, 1, 2, 0, 0, 48, None) == sk.SKGEMM_EINVAL
+    assert lib.skgemm_mxfp4_batched(a, a, a, a, 2, 16, 128, 1, 2, 0, 7, 16, 48, None) == sk.SKGEMM_EINVAL
+    assert lib.skgemm_reserve_batched(1, 16, 1, 0, None) == sk.SKGEMM_EINVAL
     # the streaming-read reference
     assert lib.skgemm_read_probe(None, 64, a, None) == sk.SKGEMM_EINVAL
     assert lib.skgemm_read_probe(a, 24, a, None) == sk.SKGEMM_EINVAL

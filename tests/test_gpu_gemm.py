@@ -388,6 +388,83 @@ def test_wide_integer_exact(S, monkeypatch):
         assert np.array_equal(F.bf16_bits_to_f64(run_bf16(x, w, S)), F.bf16_bits_to_f64(want))
 
 
+BATCH_KINDS = [("2", [(3, 512, 1024, 4), (16, 256, 2048, 2)]),   # cluster
+               ("1", [(8, 2048, 4096, 4), (24, 1024, 2048, 8)]),  # stream
+               ("3", [(40, 512, 4096, 4), (128, 256, 2048, 2)]),  # wide
+               ("0", [(5, 160, 512, 2), (70, 64, 1024, 4)])]      # tiled
+
+
+@pytest.mark.parametrize("kind,cases", BATCH_KINDS, ids=["cluster", "stream", "wide", "tiled"])
+def test_batched_bf16(kind, cases, monkeypatch):
+    """L problems in one launch equal L single calls: every problem against
+    the oracle, padded strides (gaps in C untouched), L = 1 bit-equal to the
+    single call, and weights shared across the batch (stride 0)."""
+    monkeypatch.setenv("SKGEMM_KIND", kind)
+    t = torch()
+    for (T, N, K, S) in cases:
+        L = 3
+        log(f"batched kind={kind} L={L} T={T} N={N} K={K} S={S} tactic={sk.skgemm_tactic_for(T, N, K, S)}")
+        xs, ws = zip(*[workloads.small_bf16_case(T, K, N, seed=9300 + 7 * l + T) for l in range(L)])
+        wpad, xpad, cpad = 256, 512, 64  # elements of padding after each problem
+        Wb = t.zeros(L, N * K + wpad, dtype=t.int16, device=DEV)
+        Xb = t.zeros(L, T * K + xpad, dtype=t.int16, device=DEV)
+        for l in range(L):
+            Wb[l, :N * K] = to_dev_bf16(ws[l]).view(t.int16).reshape(-1)
+            Xb[l, :T * K] = to_dev_bf16(xs[l]).view(t.int16).reshape(-1)
+        sentinel = 0x7FC1
+        Cb = t.full((L, T * N + cpad), sentinel, dtype=t.int16, device=DEV)
+        sk.skgemm_bf16_batched(Wb, Xb, Cb, T, N, K, S, L, (N * K + wpad) * 2, (T * K + xpad) * 2,
+                               (T * N + cpad) * 2)
+        t.cuda.synchronize()
+        cb = Cb.cpu().numpy().view(np.uint16)
+        assert np.all(cb[:, T * N:] == sentinel)
+        for l in range(L):
+            assert_parity(cb[l, :T * N].reshape(T, N), G.gemm_bf16_ref(xs[l], ws[l]), K, f"batch {l}")
+        # L = 1 is the single call, bit for bit
+        one = t.empty((T, N), dtype=t.bfloat16, device=DEV)
+        sk.skgemm_bf16_batched(Wb, Xb, one, T, N, K, S, 1, 0, 0, 0)
+        t.cuda.synchronize()
+        single = run_bf16(xs[0], ws[0], S)
+        assert np.array_equal(bf16_bits(one), single)
+        # weights shared by every problem
+        Cs = t.empty((L, T * N), dtype=t.bfloat16, device=DEV)
+        sk.skgemm_bf16_batched(Wb, Xb, Cs, T, N, K, S, L, 0, (T * K + xpad) * 2, T * N * 2)
+        t.cuda.synchronize()
+        cs = bf16_bits(Cs)
+        for l in range(L):
+            assert_parity(cs[l].reshape(T, N), G.gemm_bf16_ref(xs[l], ws[0]), K, f"shared W, batch {l}")
+
+
+def test_batched_mxfp4_and_oversized_grid():
+    """MXFP4 batches, and a batch whose grid exceeds what the GPU holds at once
+    (owners then hand over at once): still one correct result per problem."""
+    t = torch()
+    for (T, N, K, S, L) in [(16, 512, 2048, 4, 3), (48, 512, 2048, 4, 12)]:
+        log(f"batched mxfp4 L={L} T={T} N={N} K={K} S={S} tactic={sk.skgemm_tactic_for(T, N, K, S, True)}")
+        cases = [workloads.small_mxfp4_case(T, K, N, seed=9400 + l) for l in range(L)]
+        Wq = to_dev_u8(np.stack([c[1] for c in cases]))
+        Ws = to_dev_u8(np.stack([c[2] for c in cases]))
+        X = to_dev_bf16(np.stack([c[0] for c in cases]))
+        C = t.empty((L, T, N), dtype=t.bfloat16, device=DEV)
+        sk.skgemm_mxfp4_batched(Wq, Ws, X, C, T, N, K, S, L, N * K // 2, N * K // 32, T * K * 2, T * N * 2)
+        t.cuda.synchronize()
+        cb = bf16_bits(C)
+        for l, (x, wq, ws) in enumerate(cases):
+            assert_parity(cb[l], G.gemm_mxfp4_ref(x, wq, ws), K, f"mx batch {l}")
+    for (T, N, K, S, L) in [(64, 1024, 2048, 4, 40)]:  # wide kernel, 640 workgroups
+        log(f"batched bf16 oversized L={L} T={T} N={N} K={K} S={S} tactic={sk.skgemm_tactic_for(T, N, K, S)}")
+        cases = [workloads.small_bf16_case(T, K, N, seed=9500 + l) for l in range(L)]
+        W = to_dev_bf16(np.stack([c[1] for c in cases]))
+        X = to_dev_bf16(np.stack([c[0] for c in cases]))
+        C = t.empty((L, T, N), dtype=t.bfloat16, device=DEV)
+        sk.skgemm_bf16_batched(W, X, C, T, N, K, S, L, N * K * 2, T * K * 2, T * N * 2)
+        t.cuda.synchronize()
+        cb = bf16_bits(C)
+        for l in (0, 7, L - 1):
+            x, w = cases[l]
+            assert_parity(cb[l], G.gemm_bf16_ref(x, w), K, f"oversized batch {l}")
+
+
 def test_timeline_stamps(monkeypatch):
     """Opt-in phase stamps: five non-decreasing device-clock values per
     workgroup, results unchanged, and nothing written once turned off."""
