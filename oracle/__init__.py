@@ -8,10 +8,11 @@ path (``split_reduction_amd``), and neither side imports the other.
 What it computes (the pages are the vLLM API documentation pages listed below):
 
 * ``formats``: the number formats the path reads and writes -- bf16 with
-  round-to-nearest-even, OCP E4M3FN, E2M1 and E8M0 (MXFP4), each written from
-  the format's own definition, not from a bit trick.
+  round-to-nearest-even, OCP E4M3FN, E2M1 and E8M0 (MXFP4), and MXFP8 (E4M3
+  elements with E8M0 block scales), each written from the format's own
+  definition, not from a bit trick.
 * ``gemm``: the plain fp64 definition ``C[t, n] = sum_k X[t, k] * W[n, k]`` and
-  its MXFP4 form on decoded weights, a pure-Python brute force for tiny shapes,
+  its MXFP4 and MXFP8 forms on decoded weights, a pure-Python brute force for tiny shapes,
   the acceptance bound, and the fixed-order fp32 butterfly of a wave reduction.
 
 Pages cited in this package:

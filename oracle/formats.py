@@ -234,3 +234,38 @@ def mxfp4_dequant_bf16_bits(wq: np.ndarray, wscale: np.ndarray) -> np.ndarray:
         raise ValueError("MXFP4 decode is not exact in bf16 for these scale codes")
     # signed zeros: E2M1 -0 times a scale is -0, which the bit pattern keeps
     return bits
+
+
+def mxfp8_dequant_f64(wq8: np.ndarray, wscale: np.ndarray) -> np.ndarray:
+    """MXFP8 weights -> float64 [N, K]: w[n, k] = E4M3(wq8[n, k]) * 2**(s[n, k//32] - 127).
+
+    ``wq8`` is uint8 [N, K], one OCP E4M3FN code per byte (element k in byte
+    k); ``wscale`` is uint8 [N, K/32], one E8M0 code per 32-element K block.
+    This is the block scaling of the MXFP4 path (page
+    vllm.models.muse_spark.amd.mono.kernels.dev, e8m0_f32) with eight-bit E4M3
+    elements, the format of that page family's fp8_pack4 helper (page
+    vllm.models.deepseek_v41.amd.mono.common.ops). Code 0x7F / 0xFF is NaN.
+    """
+    codes = np.asarray(wq8, dtype=np.uint8)
+    n, k = codes.shape
+    wscale = np.asarray(wscale, dtype=np.uint8)
+    if wscale.shape != (n, k // 32) or k % 32:
+        raise ValueError(f"scale shape {wscale.shape} does not match weights [{n}, {k}]")
+    scale = np.repeat(e8m0_value(wscale), 32, axis=1)
+    return e4m3_value(codes) * scale
+
+
+def mxfp8_dequant_bf16_bits(wq8: np.ndarray, wscale: np.ndarray) -> np.ndarray:
+    """MXFP8 weights -> bf16 bit patterns [N, K], requiring the result to be exact.
+
+    E4M3 values have at most four significant bits, so every product with a
+    power of two that stays normal and finite is a bf16 value; the rounding
+    below is then the identity, which is asserted (NaN codes stay NaN).
+    """
+    w = mxfp8_dequant_f64(wq8, wscale)
+    bits = f32_to_bf16_rne(w.astype(np.float32))
+    back = bf16_bits_to_f64(bits)
+    both_nan = np.isnan(back) & np.isnan(w)
+    if not np.all((back == w) | both_nan):
+        raise ValueError("MXFP8 decode is not exact in bf16 for these scale codes")
+    return bits

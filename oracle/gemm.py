@@ -29,7 +29,7 @@ import math
 
 import numpy as np
 
-from .formats import bf16_bits_to_f64, mxfp4_dequant_f64
+from .formats import bf16_bits_to_f64, mxfp4_dequant_f64, mxfp8_dequant_f64
 
 
 def gemm_bf16_ref(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
@@ -50,6 +50,15 @@ def gemm_mxfp4_ref(x_bits: np.ndarray, wq: np.ndarray, wscale: np.ndarray) -> np
     """C[T, N] float64 = X . dequant(Wq, Wscale)^T."""
     x = bf16_bits_to_f64(x_bits)
     w = mxfp4_dequant_f64(wq, wscale)
+    if x.shape[1] != w.shape[1]:
+        raise ValueError(f"shape mismatch X{x.shape} W{w.shape}")
+    return x @ w.T
+
+
+def gemm_mxfp8_ref(x_bits: np.ndarray, wq8: np.ndarray, wscale: np.ndarray) -> np.ndarray:
+    """C[T, N] float64 = X . dequant(Wq8, Wscale)^T (E4M3 elements, E8M0 block scales)."""
+    x = bf16_bits_to_f64(x_bits)
+    w = mxfp8_dequant_f64(wq8, wscale)
     if x.shape[1] != w.shape[1]:
         raise ValueError(f"shape mismatch X{x.shape} W{w.shape}")
     return x @ w.T

@@ -221,3 +221,70 @@ def test_pins_catch_planted_mistakes():
     assert list(F.e2m1_value(swapped[0, :8])) != [0, 0.5, 1, 1.5, 2, 3, 4, 6]
     # a scale bias of 128 instead of 127 fails the E8M0 closed form
     assert F.e8m0_value(np.array([127]))[0] == 1.0 != 2.0 ** (127 - 128)
+
+
+def _e4m3_fields(code: int) -> float:
+    """E4M3FN from its bit fields, written out for the pins below."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 7
+    if e == 15 and m == 7:
+        return math.nan
+    if e == 0:
+        return sign * m * 2.0 ** -9
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def test_mxfp8_golden_cases():
+    for row in golden_rows("mxfp8_cases.txt"):
+        codes = [int(b, 16) for b in row[:8]]
+        scale = int(row[8])
+        vals = [float(v) for v in row[9:]]
+        wq8 = np.tile(np.array(codes, dtype=np.uint8), 4).reshape(1, 32)
+        got = F.mxfp8_dequant_f64(wq8, np.array([[scale]], dtype=np.uint8))[0, :8]
+        for g, v in zip(got, vals):
+            if math.isnan(v):
+                assert math.isnan(g)
+            else:
+                assert g == v and math.copysign(1.0, g) == math.copysign(1.0, v), (row, list(got))
+
+
+def test_mxfp8_bruteforce_small():
+    rng = np.random.default_rng(12)
+    n, k = 3, 96
+    wq8 = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
+    ws = rng.integers(110, 140, size=(n, k // 32), dtype=np.uint8)
+    got = F.mxfp8_dequant_f64(wq8, ws)
+    for r in range(n):
+        for c in range(k):
+            want = _e4m3_fields(int(wq8[r][c])) * 2.0 ** (int(ws[r][c // 32]) - 127)
+            if math.isnan(want):
+                assert math.isnan(got[r][c])
+            else:
+                assert got[r][c] == want
+
+
+def test_mxfp8_bf16_exact_range():
+    # every non-NaN code with every scale in [10, 246] decodes exactly to bf16
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    codes = np.concatenate([codes, codes[: (-len(codes)) % 32]])
+    scales = np.arange(10, 247, dtype=np.uint8)
+    n, k = len(scales), len(codes)
+    wq8 = np.tile(codes, (n, 1))
+    ws = np.repeat(scales.reshape(n, 1), k // 32, axis=1)
+    vals = F.bf16_bits_to_f64(F.mxfp8_dequant_bf16_bits(wq8, ws))
+    expect = np.array([[_e4m3_fields(int(c)) * 2.0 ** (int(sc) - 127) for c in codes] for sc in scales])
+    assert np.array_equal(vals, expect)
+
+
+def test_mxfp8_planted_mistakes_fail():
+    """A decode that reads codes as E5M2, or applies the scale of the wrong
+    block, must differ from the oracle on the golden rows."""
+    wq8 = np.tile(np.array([0x38, 0x40, 0x48, 0x30, 0x3C, 0x01, 0x08, 0x7E], dtype=np.uint8), 8).reshape(1, 64)
+    ws = np.array([[127, 129]], dtype=np.uint8)
+    good = F.mxfp8_dequant_f64(wq8, ws)
+    wrong_block = F.e4m3_value(wq8) * np.ldexp(1.0, np.repeat(ws[:, ::-1].astype(int) - 127, 32, axis=1))
+    assert not np.array_equal(good, wrong_block)
+    e5m2 = np.array([[(-1.0) ** (int(c) >> 7) * (1 + (int(c) & 3) / 4) * 2.0 ** (((int(c) >> 2) & 31) - 15) for c in row]
+                     for row in wq8])
+    assert not np.allclose(good[:, :32], e5m2[:, :32])

@@ -126,3 +126,21 @@ def test_butterfly_integer_sum_exact():
     v = rng.integers(-1000, 1000, size=(50, 64)).astype(np.float32)
     out = G.butterfly_f32(v)
     assert np.array_equal(out, np.repeat(v.sum(axis=1, dtype=np.float64)[:, None], 64, axis=1))
+
+
+def test_mxfp8_gemm_matches_bruteforce_and_integer_exact():
+    """The MXFP8 GEMM on decoded weights equals the pure-Python triple loop,
+    and with integer E4M3 values, integer X and scale 1 it is exact."""
+    rng = np.random.default_rng(21)
+    T, N, K = 2, 3, 64
+    ints = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0, 0xC4], dtype=np.uint8)  # 0 1 2 3 4 -1 -2 -3
+    wq8 = rng.choice(ints, size=(N, K))
+    ws = np.full((N, K // 32), 127, dtype=np.uint8)
+    xv = rng.integers(-3, 4, size=(T, K)).astype(np.float32)
+    x = F.f32_to_bf16_rne(xv)
+    got = G.gemm_mxfp8_ref(x, wq8, ws)
+    wv = F.mxfp8_dequant_f64(wq8, ws)
+    assert set(np.unique(wv)) <= {0.0, 1.0, 2.0, 3.0, 4.0, -1.0, -2.0, -3.0}
+    bf = G.gemm_bruteforce(F.bf16_bits_to_f64(x).tolist(), wv.tolist())
+    assert np.array_equal(got, np.array(bf))
+    assert np.array_equal(got, np.round(got))
