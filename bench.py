@@ -99,8 +99,9 @@ class Case:
         self.x_bits = x
         self.X = torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
         self.C = torch.empty((wl.T, wl.N), dtype=torch.bfloat16, device=dev)
-        if wl.kind == "mxfp4":
-            wq, ws = host_w if host_w is not None else workloads.gen_w_mxfp4(wl)
+        if wl.kind in ("mxfp4", "mxfp8"):
+            gen = workloads.gen_w_mxfp4 if wl.kind == "mxfp4" else workloads.gen_w_mxfp8
+            wq, ws = host_w if host_w is not None else gen(wl)
             base = (torch.from_numpy(wq).to(dev), torch.from_numpy(ws).to(dev))
         else:
             wb = host_w if host_w is not None else workloads.gen_w_bf16(wl)
@@ -115,6 +116,8 @@ class Case:
         w = self.weights[i % len(self.weights)]
         if wl.kind == "mxfp4":
             sk.skgemm_mxfp4(w[0], w[1], self.X, self.C, wl.T, wl.N, wl.K, wl.split_k, stream)
+        elif wl.kind == "mxfp8":
+            sk.skgemm_mxfp8(w[0], w[1], self.X, self.C, wl.T, wl.N, wl.K, wl.split_k, stream)
         else:
             sk.skgemm_bf16(w[0], self.X, self.C, wl.T, wl.N, wl.K, wl.split_k, stream)
 
@@ -179,7 +182,7 @@ class Case:
         wq = torch.empty((R, L) + tuple(base[0].shape), dtype=base[0].dtype, device=dev)
         wq.copy_(base[0].expand(R, L, *base[0].shape))
         ws = None
-        if wl.kind == "mxfp4":
+        if wl.kind in ("mxfp4", "mxfp8"):
             ws = torch.empty((R, L) + tuple(base[1].shape), dtype=base[1].dtype, device=dev)
             ws.copy_(base[1].expand(R, L, *base[1].shape))
         X = self.X.expand(L, *self.X.shape).contiguous()
@@ -192,9 +195,10 @@ class Case:
 
         def launch(i, st):
             r = i % R
-            if wl.kind == "mxfp4":
-                sk.skgemm_mxfp4_batched(wq[r], ws[r], X, C, wl.T, wl.N, wl.K, wl.split_k, L, wstride,
-                                        base[1].numel(), xstride, cstride, st)
+            if wl.kind in ("mxfp4", "mxfp8"):
+                fn = sk.skgemm_mxfp4_batched if wl.kind == "mxfp4" else sk.skgemm_mxfp8_batched
+                fn(wq[r], ws[r], X, C, wl.T, wl.N, wl.K, wl.split_k, L, wstride, base[1].numel(), xstride,
+                   cstride, st)
             else:
                 sk.skgemm_bf16_batched(wq[r], X, C, wl.T, wl.N, wl.K, wl.split_k, L, wstride, xstride,
                                        cstride, st)
@@ -245,7 +249,7 @@ def run_workload(wl, steps, warmup, host_w=None) -> dict:
     probe = case.time(steps, warmup, rotate=True, probe=True)
     probe_bytes = case.weights[0][0].numel() * case.weights[0][0].element_size()
     probe_tbps = probe_bytes / (probe["t_us"] * 1e-6) / 1e12
-    tac = sk.skgemm_tactic_for(wl.T, wl.N, wl.K, wl.split_k, wl.kind == "mxfp4")
+    tac = sk.skgemm_tactic_for(wl.T, wl.N, wl.K, wl.split_k, {"bf16": 0, "mxfp4": 1, "mxfp8": 2}[wl.kind])
     out = {
         "workload": wl.name, "kind": wl.kind, "T": wl.T, "K": wl.K, "N": wl.N,
         "split_k": wl.split_k, "weight_bytes": wl.weight_bytes(), "flops": wl.flops(),
@@ -508,7 +512,8 @@ def main() -> None:
     if not args.only_headline:
         steps = max(20, args.steps // 2)
         warm = max(3, args.warmup // 2)
-        for name in ("bf16_t1_k1024_n1024", "bf16_t32_k7168_n18432", "mxfp4_t16_k7168_n4096"):
+        for name in ("bf16_t1_k1024_n1024", "bf16_t32_k7168_n18432", "mxfp4_t16_k7168_n4096",
+                     "mxfp8_t16_k7168_n4096"):
             log(f"workload {name}")
             r = run_workload(workloads.WORKLOADS[name], steps, warm)
             log(json.dumps({k: v for k, v in r.items() if not k.startswith("_")}))

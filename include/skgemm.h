@@ -97,7 +97,24 @@ SKGEMM_API int skgemm_mxfp4(const void* Wq, const void* Wscale, const void* X, v
                             int N, int K, int split_k, hipStream_t stream);
 
 /*
- * skgemm_bf16_batched, skgemm_mxfp4_batched: L independent problems of one
+ * skgemm_mxfp8: C = X . dequant(Wq8, Wscale)^T with MXFP8 weights: one OCP
+ * E4M3FN code per byte, Wq8 uint8 [N, K] row-major (element k of a row in
+ * byte k), and one E8M0 scale code per 32-element K block, Wscale uint8
+ * [N, K/32]. w[n, k] = E4M3(code) * 2^(scale - 127), decoded exactly to bf16
+ * in registers (v_cvt_scalef32_pk_bf16_fp8) and multiplied as in skgemm_bf16:
+ * the block scaling of skgemm_mxfp4 (page
+ * vllm.models.muse_spark.amd.mono.kernels.dev, e8m0_f32) with the E4M3
+ * elements of page vllm.models.deepseek_v41.amd.mono.common.ops, fp8_pack4.
+ *   Wq8, X, C 16-byte aligned; Wscale needs no alignment.
+ *   K % (64 * split_k) == 0 (each lane decodes 16 consecutive K elements,
+ *   half a scale block, per 16-byte load). Other arguments as skgemm_bf16.
+ */
+SKGEMM_API int skgemm_mxfp8(const void* Wq8, const void* Wscale, const void* X, void* C, int T,
+                            int N, int K, int split_k, hipStream_t stream);
+
+/*
+ * skgemm_bf16_batched, skgemm_mxfp4_batched, skgemm_mxfp8_batched: L
+ * independent problems of one
  * shape in one launch (the pages' batch dimension L: SplitKGemm.kernel takes
  * A (M,K,L), B (N,K,L), C (M,N,L) and SplitKGemm.__call__ launches the L
  * problems as the third grid dimension). Problem l reads W + l*w_stride, X + l*x_stride (and Wscale +
@@ -116,6 +133,10 @@ SKGEMM_API int skgemm_bf16_batched(const void* W, const void* X, void* C, int T,
                                    size_t c_stride, hipStream_t stream);
 SKGEMM_API int skgemm_mxfp4_batched(const void* Wq, const void* Wscale, const void* X, void* C,
                                     int T, int N, int K, int split_k, int L, size_t wq_stride,
+                                    size_t wscale_stride, size_t x_stride, size_t c_stride,
+                                    hipStream_t stream);
+SKGEMM_API int skgemm_mxfp8_batched(const void* Wq8, const void* Wscale, const void* X, void* C,
+                                    int T, int N, int K, int split_k, int L, size_t wq8_stride,
                                     size_t wscale_stride, size_t x_stride, size_t c_stride,
                                     hipStream_t stream);
 
@@ -147,6 +168,16 @@ SKGEMM_API int skgemm_release(void);
  * bit-exact testing). K % 32 == 0, Wq and W_out 16-byte aligned.
  */
 SKGEMM_API int skgemm_mxfp4_dequant(const void* Wq, const void* Wscale, void* W_out, int N, int K,
+                                    hipStream_t stream);
+
+/*
+ * skgemm_mxfp8_dequant: W_out bf16 [N, K] = E4M3(Wq8) * 2^(Wscale - 127),
+ * the in-register decode of skgemm_mxfp8 on its own (bit-exact tests).
+ * Exact for scale codes 10..246 (every product then normal and finite in
+ * bf16); codes 0x7F and 0xFF give NaN. K % 32 == 0; Wq8 and W_out 16-byte
+ * aligned.
+ */
+SKGEMM_API int skgemm_mxfp8_dequant(const void* Wq8, const void* Wscale, void* W_out, int N, int K,
                                     hipStream_t stream);
 
 /*
@@ -182,19 +213,21 @@ SKGEMM_API int skgemm_wave_sum(const float* in, float* out, size_t n_waves, hipS
  * block, and computes nothing from them. The time it takes is the
  * streaming-read rate the GEMM kernels are compared with at the same byte
  * count. src: 16-byte aligned, bytes a multiple of 16. sink: device memory for
- * 512 uint32 words, which the probe does not normally write. Returns SKGEMM_EINVAL for a null pointer or a bad size,
- * SKGEMM_EALIGN for misaligned pointers.
+ * 512 uint32 words, which the probe does not normally write. Returns
+ * SKGEMM_EINVAL for a null pointer or a bad size, SKGEMM_EALIGN for
+ * misaligned pointers.
  */
 SKGEMM_API int skgemm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 /*
  * skgemm_tactic_for: describe, as a short JSON object written to buf
  * (NUL-terminated, truncated to buf_len), the kernel configuration a call with
- * these sizes would launch. mxfp4 != 0 selects the MXFP4 entry point. Returns
+ * these sizes would launch. weight_format: 0 bf16 (skgemm_bf16), 1 MXFP4
+ * (skgemm_mxfp4), 2 MXFP8 (skgemm_mxfp8); SKGEMM_EINVAL for others. Returns
  * the same code the compute call's argument checks would (pointers excluded).
  * Host only; touches no device.
  */
-SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int mxfp4, char* buf,
+SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int weight_format, char* buf,
                                  size_t buf_len);
 
 /*

@@ -40,6 +40,9 @@ def _declare(lib):
     sig = {
         "skgemm_bf16": [vp, vp, vp, i, i, i, i, st],
         "skgemm_mxfp4": [vp, vp, vp, vp, i, i, i, i, st],
+        "skgemm_mxfp8": [vp, vp, vp, vp, i, i, i, i, st],
+        "skgemm_mxfp8_batched": [vp, vp, vp, vp, i, i, i, i, i, sz, sz, sz, sz, st],
+        "skgemm_mxfp8_dequant": [vp, vp, vp, i, i, st],
         "skgemm_reserve": [i, i, i, st],
         "skgemm_reserve_batched": [i, i, i, i, st],
         "skgemm_bf16_batched": [vp, vp, vp, i, i, i, i, i, sz, sz, sz, st],
@@ -145,6 +148,25 @@ def skgemm_mxfp4_batched(Wq, Wscale, X, C, T: int, N: int, K: int, split_k: int,
     _check(code, "skgemm_mxfp4_batched")
 
 
+def skgemm_mxfp8(Wq8, Wscale, X, C, T: int, N: int, K: int, split_k: int, stream=None) -> None:
+    """C = X . dequant(Wq8, Wscale)^T with E4M3 weights and E8M0 block scales."""
+    code = lib().skgemm_mxfp8(_ptr(Wq8), _ptr(Wscale), _ptr(X), _ptr(C), T, N, K, split_k, _stream(stream))
+    _check(code, "skgemm_mxfp8")
+
+
+def skgemm_mxfp8_batched(Wq8, Wscale, X, C, T: int, N: int, K: int, split_k: int, L: int, wq8_stride: int,
+                         wscale_stride: int, x_stride: int, c_stride: int, stream=None) -> None:
+    """L MXFP8 problems of one shape in one launch; strides in bytes."""
+    code = lib().skgemm_mxfp8_batched(_ptr(Wq8), _ptr(Wscale), _ptr(X), _ptr(C), T, N, K, split_k, L,
+                                      wq8_stride, wscale_stride, x_stride, c_stride, _stream(stream))
+    _check(code, "skgemm_mxfp8_batched")
+
+
+def skgemm_mxfp8_dequant(Wq8, Wscale, W_out, N: int, K: int, stream=None) -> None:
+    code = lib().skgemm_mxfp8_dequant(_ptr(Wq8), _ptr(Wscale), _ptr(W_out), N, K, _stream(stream))
+    _check(code, "skgemm_mxfp8_dequant")
+
+
 def skgemm_reserve_batched(max_T: int, max_N: int, max_split_k: int, max_L: int, stream=None) -> None:
     _check(lib().skgemm_reserve_batched(max_T, max_N, max_split_k, max_L, _stream(stream)),
            "skgemm_reserve_batched")
@@ -175,10 +197,11 @@ def skgemm_wave_sum(inp, out, n_waves: int, stream=None) -> None:
     _check(lib().skgemm_wave_sum(_ptr(inp), _ptr(out), n_waves, _stream(stream)), "skgemm_wave_sum")
 
 
-def skgemm_tactic_for(T: int, N: int, K: int, split_k: int, mxfp4: bool = False) -> dict:
-    """The launch configuration a call with these sizes uses (host only)."""
+def skgemm_tactic_for(T: int, N: int, K: int, split_k: int, weight_format: int = 0) -> dict:
+    """The launch configuration a call with these sizes uses (host only).
+    weight_format: 0 bf16, 1 MXFP4 (True also means MXFP4), 2 MXFP8."""
     buf = ctypes.create_string_buffer(512)
-    code = lib().skgemm_tactic_for(T, N, K, split_k, 1 if mxfp4 else 0, buf, len(buf))
+    code = lib().skgemm_tactic_for(T, N, K, split_k, int(weight_format), buf, len(buf))
     _check(code, "skgemm_tactic_for")
     return json.loads(buf.value.decode())
 

@@ -13,6 +13,7 @@
 
 #include "skgemm.h"
 #include "skgemm_internal.h"
+#include "device/wfmt.h"
 
 namespace {
 
@@ -40,14 +41,19 @@ int hip_fail(hipError_t e) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Argument checks shared by both GEMM entry points and the tactic query.
+// K granularity of one split rank's slice per weight format: a load step of
+// 32 bf16 elements, or four lanes' 16-byte pieces of block-scaled codes.
+int k_step(int wf) { return wf == skg::kBf16 ? 32 : 4 * skg::lane_k(wf); }
+
+// Argument checks shared by the GEMM entry points and the tactic query.
 // Pointers are checked only when check_ptrs is set.
-int check_gemm(bool mx, const void* w, const void* ws, const void* x, const void* c, int T, int N,
+int check_gemm(int wf, const void* w, const void* ws, const void* x, const void* c, int T, int N,
                int K, int S, bool check_ptrs) {
+  const bool mx = wf != skg::kBf16;
   if (T < 0 || N < 0 || K < 0) return SKGEMM_EINVAL;
   if (S != 1 && S != 2 && S != 4 && S != 8) return SKGEMM_EINVAL;
   if (N % 16 != 0) return SKGEMM_ESHAPE;
-  if (K % ((mx ? 128 : 32) * S) != 0) return SKGEMM_ESHAPE;
+  if (K % (k_step(wf) * S) != 0) return SKGEMM_ESHAPE;
   if (N > SKGEMM_MAX_N || K > SKGEMM_MAX_K) return SKGEMM_ESHAPE;
   if (!check_ptrs || T == 0 || N == 0) return SKGEMM_OK;
   if (c == nullptr) return SKGEMM_EINVAL;
@@ -150,9 +156,9 @@ int check_batch(const Batch& b, int T, int N) {
   return SKGEMM_OK;
 }
 
-int run_gemm(bool mx, const void* w, const void* ws, const void* x, void* c, int T, int N, int K,
+int run_gemm(int wf, const void* w, const void* ws, const void* x, void* c, int T, int N, int K,
              int S, hipStream_t stream, const Batch& batch = Batch{}) {
-  int rc = check_gemm(mx, w, ws, x, c, T, N, K, S, true);
+  int rc = check_gemm(wf, w, ws, x, c, T, N, K, S, true);
   if (rc != SKGEMM_OK) return rc;
   rc = check_batch(batch, T, N);
   if (rc != SKGEMM_OK) return rc;
@@ -167,7 +173,7 @@ int run_gemm(bool mx, const void* w, const void* ws, const void* x, void* c, int
   for (int t0 = 0; t0 < T; t0 += kTokenBlock) {
     const int tb = std::min(kTokenBlock, T - t0);
     skg::Tactic tac{};
-    if (!skg::pick_tactic(tb, N, K, S, mx, &tac, L)) return SKGEMM_ESHAPE;
+    if (!skg::pick_tactic(tb, N, K, S, wf, &tac, L)) return SKGEMM_ESHAPE;
     skg::GemmParams p{};
     p.w = w;
     p.wscale = static_cast<const uint8_t*>(ws);
@@ -207,12 +213,17 @@ extern "C" {
 
 SKGEMM_API int skgemm_bf16(const void* W, const void* X, void* C, int T, int N, int K,
                            int split_k, hipStream_t stream) {
-  return run_gemm(false, W, nullptr, X, C, T, N, K, split_k, stream);
+  return run_gemm(skg::kBf16, W, nullptr, X, C, T, N, K, split_k, stream);
 }
 
 SKGEMM_API int skgemm_mxfp4(const void* Wq, const void* Wscale, const void* X, void* C, int T,
                             int N, int K, int split_k, hipStream_t stream) {
-  return run_gemm(true, Wq, Wscale, X, C, T, N, K, split_k, stream);
+  return run_gemm(skg::kMxfp4, Wq, Wscale, X, C, T, N, K, split_k, stream);
+}
+
+SKGEMM_API int skgemm_mxfp8(const void* Wq8, const void* Wscale, const void* X, void* C, int T,
+                            int N, int K, int split_k, hipStream_t stream) {
+  return run_gemm(skg::kMxfp8, Wq8, Wscale, X, C, T, N, K, split_k, stream);
 }
 
 SKGEMM_API int skgemm_bf16_batched(const void* W, const void* X, void* C, int T, int N, int K,
@@ -223,7 +234,7 @@ SKGEMM_API int skgemm_bf16_batched(const void* W, const void* X, void* C, int T,
   b.bw = w_stride;
   b.bx = x_stride;
   b.bc = c_stride;
-  return run_gemm(false, W, nullptr, X, C, T, N, K, split_k, stream, b);
+  return run_gemm(skg::kBf16, W, nullptr, X, C, T, N, K, split_k, stream, b);
 }
 
 SKGEMM_API int skgemm_mxfp4_batched(const void* Wq, const void* Wscale, const void* X, void* C,
@@ -236,7 +247,20 @@ SKGEMM_API int skgemm_mxfp4_batched(const void* Wq, const void* Wscale, const vo
   b.bws = wscale_stride;
   b.bx = x_stride;
   b.bc = c_stride;
-  return run_gemm(true, Wq, Wscale, X, C, T, N, K, split_k, stream, b);
+  return run_gemm(skg::kMxfp4, Wq, Wscale, X, C, T, N, K, split_k, stream, b);
+}
+
+SKGEMM_API int skgemm_mxfp8_batched(const void* Wq8, const void* Wscale, const void* X, void* C,
+                                    int T, int N, int K, int split_k, int L, size_t wq8_stride,
+                                    size_t wscale_stride, size_t x_stride, size_t c_stride,
+                                    hipStream_t stream) {
+  Batch b;
+  b.L = L;
+  b.bw = wq8_stride;
+  b.bws = wscale_stride;
+  b.bx = x_stride;
+  b.bc = c_stride;
+  return run_gemm(skg::kMxfp8, Wq8, Wscale, X, C, T, N, K, split_k, stream, b);
 }
 
 SKGEMM_API int skgemm_reserve(int max_T, int max_N, int max_split_k, hipStream_t stream) {
@@ -278,6 +302,17 @@ SKGEMM_API int skgemm_mxfp4_dequant(const void* Wq, const void* Wscale, void* W_
   return e == hipSuccess ? SKGEMM_OK : hip_fail(e);
 }
 
+SKGEMM_API int skgemm_mxfp8_dequant(const void* Wq8, const void* Wscale, void* W_out, int N, int K,
+                                    hipStream_t stream) {
+  if (N < 0 || K < 0) return SKGEMM_EINVAL;
+  if (K % 32 != 0) return SKGEMM_ESHAPE;
+  if (N == 0 || K == 0) return SKGEMM_OK;
+  if (!Wq8 || !Wscale || !W_out) return SKGEMM_EINVAL;
+  if (!aligned16(Wq8) || !aligned16(W_out)) return SKGEMM_EALIGN;
+  hipError_t e = skg::launch_mxfp8_dequant(Wq8, Wscale, W_out, N, K, stream);
+  return e == hipSuccess ? SKGEMM_OK : hip_fail(e);
+}
+
 SKGEMM_API int skgemm_pack_bf16(const float* in, uint32_t* out, size_t n_pairs, hipStream_t stream) {
   if (n_pairs == 0) return SKGEMM_OK;
   if (!in || !out) return SKGEMM_EINVAL;
@@ -302,22 +337,23 @@ SKGEMM_API int skgemm_wave_sum(const float* in, float* out, size_t n_waves, hipS
   return e == hipSuccess ? SKGEMM_OK : hip_fail(e);
 }
 
-SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int mxfp4, char* buf,
+SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int weight_format, char* buf,
                                  size_t buf_len) {
-  const bool mx = mxfp4 != 0;
-  int rc = check_gemm(mx, nullptr, nullptr, nullptr, nullptr, T, N, K, split_k, false);
+  if (weight_format < skg::kBf16 || weight_format > skg::kMxfp8) return SKGEMM_EINVAL;
+  int rc = check_gemm(weight_format, nullptr, nullptr, nullptr, nullptr, T, N, K, split_k, false);
   if (rc != SKGEMM_OK) return rc;
   skg::Tactic t{};
   const int tb = std::min(std::max(T, 1), kTokenBlock);
-  if (!skg::pick_tactic(tb, N, K, split_k, mx, &t)) return SKGEMM_ESHAPE;
+  if (!skg::pick_tactic(tb, N, K, split_k, weight_format, &t)) return SKGEMM_ESHAPE;
   const int blocks = (T + kTokenBlock - 1) / kTokenBlock;
   if (buf != nullptr && buf_len > 0) {
     snprintf(buf, buf_len,
              "{\"nt\": %d, \"rg\": %d, \"wk\": %d, \"wn\": %d, \"d\": %d, \"c\": %d, \"kc\": %d, "
              "\"tile_n\": %d, \"threads\": %d, \"lds\": %d, \"grid\": %d, \"split_k\": %d, "
-             "\"token_blocks\": %d, \"mxfp4\": %d, \"kind\": \"%s\", \"shape\": %d, \"fold\": %d}",
+             "\"token_blocks\": %d, \"mxfp4\": %d, \"weight_format\": %d, \"kind\": \"%s\", "
+             "\"shape\": %d, \"fold\": %d}",
              t.nt, t.rg, t.wk, t.wn, t.d, t.c, t.kc, t.tile_n, t.threads, t.lds, t.grid, split_k,
-             blocks, t.mx, t.kind == 3 ? "wide" : t.kind == 2 ? "cluster" : (t.kind == 1 ? "stream" : "tiled"), t.shape,
+             blocks, t.wf == skg::kMxfp4 ? 1 : 0, t.wf, t.kind == 3 ? "wide" : t.kind == 2 ? "cluster" : (t.kind == 1 ? "stream" : "tiled"), t.shape,
              t.kind == 2 ? t.fold : 1);
   }
   return SKGEMM_OK;

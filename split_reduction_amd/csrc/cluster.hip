@@ -32,9 +32,9 @@
 // e8m0_f32).
 
 #include "device/mfma.h"
-#include "device/mxfp4.h"
 #include "device/pack.h"
 #include "device/types.h"
+#include "device/wfmt.h"
 #include "skgemm_internal.h"
 
 namespace skg {
@@ -44,7 +44,7 @@ namespace {
 constexpr int kClusterMaxRanks = 8;
 
 // Load steps kept in flight per wave (operand registers: D * (C + NT*SUBS) * 4).
-constexpr int cluster_depth(int nt, int c, bool mx) {
+constexpr int cluster_depth(int nt, int c, bool mx) {  // mx: block-scaled weights
   return mx ? (nt == 1 ? 4 : 2) : (nt == 1 ? (c == 2 ? 4 : 8) : (c == 2 ? 2 : 4));
 }
 
@@ -52,14 +52,16 @@ constexpr int cluster_depth(int nt, int c, bool mx) {
 
 // grid = N / R workgroups of 64 * WT threads; workgroup b owns weight rows
 // b*R .. b*R + R - 1 over all of K.
-template <int NT, int F, int WT, int C, bool MX>
+template <int NT, int F, int WT, int C, int WF>
 __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
   select_problem(p);
+  constexpr bool MX = WF != kBf16;            // block-scaled weights
+  constexpr int LK = lane_k(WF);              // K elements of one lane's 16-byte piece
   constexpr int R = 16 / F;                    // weight rows of the tile
   constexpr int TF = 16 / F;                   // token slots of one fold
   constexpr int LOADS = MX ? 1 : C;            // 16-byte weight loads per lane per step
-  constexpr int SUBS = MX ? 4 : C;             // MFMA K-steps per load step
-  constexpr int PIECE_K = MX ? 128 : 32 * C;   // K elements of one fold of a step
+  constexpr int SUBS = MX ? LK / 8 : C;        // MFMA K-steps per load step
+  constexpr int PIECE_K = MX ? 4 * LK : 32 * C;  // K elements of one fold of a step
   constexpr int STEP_K = F * PIECE_K;          // K elements of one load step
   constexpr int SUB_K = MX ? 8 : 32 * F;       // K distance between a lane's sub-steps
   constexpr int D = cluster_depth(NT, C, MX);
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
   const int fb = li / TF;  // B: fold of this lane's column slot
   const int tb = li % TF;  // B: token within the fold (F == 1: the token tile's column)
 
-  const uint32_t wrow_bytes = MX ? (uint32_t)(K / 2) : (uint32_t)K * 2u;
+  const uint32_t wrow_bytes = row_bytes(WF, (uint32_t)K);
   const rsrc_t wr = make_rsrc(static_cast<const uint8_t*>(p.w) + (size_t)n0 * wrow_bytes,
                               (uint32_t)R * wrow_bytes);
   const rsrc_t sr = MX ? make_rsrc(p.wscale + (size_t)n0 * (K / 32), (uint32_t)R * (uint32_t)(K / 32))
@@ -113,10 +115,10 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
   const uint32_t s_row = (uint32_t)ra * (uint32_t)(K / 32);
   // K offset of a lane's first piece within a step. bf16: piece l of the
   // lane in fold f, K block g covers ((l*F + f)*4 + g)*8 .. +7, so one load
-  // instruction covers 64*F contiguous bytes of each row. MXFP4: the lane's
-  // 32 codes cover (f*4 + g)*32 .. +31.
-  const int a_k = (fa * 4 + g) * (MX ? 32 : 8);
-  const int b_k = (fb * 4 + g) * (MX ? 32 : 8);
+  // instruction covers 64*F contiguous bytes of each row. Block-scaled: the
+  // lane's LK codes cover (f*4 + g)*LK .. +LK-1.
+  const int a_k = (fa * 4 + g) * (MX ? LK : 8);
+  const int b_k = (fb * 4 + g) * (MX ? LK : 8);
   bool b_ok[NT];
   uint32_t b_row[NT];
 #pragma unroll
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
     int ir = i + rot;
     if (ir >= n_i) ir -= n_i;
     const int kel = kbase + (sub + WR * ir) * STEP_K;
-    const uint32_t a_off = MX ? (uint32_t)((kel + a_k) / 2) : (uint32_t)(kel + a_k) * 2u;
+    const uint32_t a_off = elem_byte(WF, (uint32_t)(kel + a_k));
 #pragma unroll
     for (int l = 0; l < LOADS; ++l)
       ra_ring[slot][l] = ld16_if(ok, wr, a_row + a_off + (uint32_t)(2 * SUB_K * l));
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
     for (int s2 = 0; s2 < SUBS; ++s2) {
       bf16x8 af;
       if constexpr (MX) {
-        af = fp4x8_bf16(ra_ring[slot][0][s2], e8m0_f32(sc_ring[slot]));
+        af = decode_operand<WF>(ra_ring[slot][0], s2, e8m0_f32(sc_ring[slot]));
       } else {
         af = as_bf16x8(ra_ring[slot][s2]);
       }
@@ -244,38 +246,39 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
 
 namespace {
 
-template <int NT, int F, int WT, int C, bool MX>
+template <int NT, int F, int WT, int C, int WF>
 hipError_t launch_cluster_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((splitk_cluster_kernel<NT, F, WT, C, MX>), dim3(t.grid, p.L), dim3(t.threads), 0, s, p);
+  hipLaunchKernelGGL((splitk_cluster_kernel<NT, F, WT, C, WF>), dim3(t.grid, p.L), dim3(t.threads), 0, s, p);
   return hipGetLastError();
 }
 
-template <int NT, int F, int C, bool MX>
+template <int NT, int F, int C, int WF>
 hipError_t launch_cluster_wt(const Tactic& t, const GemmParams& p, hipStream_t s) {
   switch (t.wk) {
-    case 4: return launch_cluster_one<NT, F, 4, C, MX>(t, p, s);
-    case 8: return launch_cluster_one<NT, F, 8, C, MX>(t, p, s);
-    case 16: return launch_cluster_one<NT, F, 16, C, MX>(t, p, s);
+    case 4: return launch_cluster_one<NT, F, 4, C, WF>(t, p, s);
+    case 8: return launch_cluster_one<NT, F, 8, C, WF>(t, p, s);
+    case 16: return launch_cluster_one<NT, F, 16, C, WF>(t, p, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <int C, bool MX>
+template <int C, int WF>
 hipError_t launch_cluster_f(const Tactic& t, const GemmParams& p, hipStream_t s) {
-  if (t.nt == 2) return t.fold == 1 ? launch_cluster_wt<2, 1, C, MX>(t, p, s) : hipErrorInvalidValue;
+  if (t.nt == 2) return t.fold == 1 ? launch_cluster_wt<2, 1, C, WF>(t, p, s) : hipErrorInvalidValue;
   if (t.nt != 1) return hipErrorInvalidValue;
   switch (t.fold) {
-    case 1: return launch_cluster_wt<1, 1, C, MX>(t, p, s);
-    case 2: return launch_cluster_wt<1, 2, C, MX>(t, p, s);
-    case 4: return launch_cluster_wt<1, 4, C, MX>(t, p, s);
-    case 8: return launch_cluster_wt<1, 8, C, MX>(t, p, s);
+    case 1: return launch_cluster_wt<1, 1, C, WF>(t, p, s);
+    case 2: return launch_cluster_wt<1, 2, C, WF>(t, p, s);
+    case 4: return launch_cluster_wt<1, 4, C, WF>(t, p, s);
+    case 8: return launch_cluster_wt<1, 8, C, WF>(t, p, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool cluster_fits(int T, int N, int ks, int S, bool mx, int max_fold, int force_c, Tactic* t) {
+bool cluster_fits(int T, int N, int ks, int S, int wf, int max_fold, int force_c, Tactic* t) {
+  const bool mx = wf != kBf16;
   if (T < 1 || T > 32 || S > kClusterMaxRanks || ks <= 0) return false;
   const int nt = (T + 15) / 16;
   // Widest fold whose token slots still hold every token.
@@ -291,7 +294,7 @@ bool cluster_fits(int T, int N, int ks, int S, bool mx, int max_fold, int force_
     if (mx && c == 2) continue;  // one 16-byte MXFP4 piece is a whole step
     if (force_c > 0 && !mx && c != force_c) continue;
     for (int f = fold; f >= 1; f /= 2) {
-      const int step = f * (mx ? 128 : 32 * c);
+      const int step = f * (mx ? 4 * lane_k(wf) : 32 * c);
       if (ks % step) continue;
       const int cs = ks / step;
       // Waves: a power of two in 4..16, at least S (so S divides it), and
@@ -322,8 +325,11 @@ bool cluster_fits(int T, int N, int ks, int S, bool mx, int max_fold, int force_
 }
 
 hipError_t launch_cluster(const Tactic& t, const GemmParams& p, hipStream_t s) {
-  if (t.mx) return launch_cluster_f<1, true>(t, p, s);
-  return t.c == 2 ? launch_cluster_f<2, false>(t, p, s) : launch_cluster_f<1, false>(t, p, s);
+  switch (t.wf) {
+    case kMxfp4: return launch_cluster_f<1, kMxfp4>(t, p, s);
+    case kMxfp8: return launch_cluster_f<1, kMxfp8>(t, p, s);
+  }
+  return t.c == 2 ? launch_cluster_f<2, kBf16>(t, p, s) : launch_cluster_f<1, kBf16>(t, p, s);
 }
 
 }  // namespace skg

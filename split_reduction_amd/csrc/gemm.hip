@@ -38,9 +38,9 @@
 #include <stdlib.h>
 
 #include "device/mfma.h"
-#include "device/mxfp4.h"
 #include "device/pack.h"
 #include "device/types.h"
+#include "device/wfmt.h"
 #include "skgemm_internal.h"
 
 namespace skg {
@@ -66,14 +66,16 @@ __device__ __forceinline__ void lds_write16(uint8_t* smem, int slot, u32x4 v) {
 
 }  // namespace
 
-template <int NT, int RG, int WK, int WN, int D, int C, bool MX>
+template <int NT, int RG, int WK, int WN, int D, int C, int WF>
 __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p) {
   select_problem(p);
+  constexpr bool MX = WF != kBf16;           // block-scaled weights
+  constexpr int LK = lane_k(WF);             // K elements of one lane's 16-byte piece
   constexpr int THREADS = 64 * WK * WN;
   constexpr int TILE_N = 16 * RG * WN;
   constexpr int LOADS = MX ? 1 : C;          // 16-byte weight loads per row group per step
-  constexpr int SUBS = MX ? 4 : C;           // MFMA K-steps per load step
-  constexpr int STEP_K = MX ? 128 : 32 * C;  // K elements of one load step
+  constexpr int SUBS = MX ? LK / 8 : C;      // MFMA K-steps per load step
+  constexpr int STEP_K = MX ? 4 * LK : 32 * C;  // K elements of one load step
   constexpr int XBATCH = 4;                  // staging loads issued before their LDS writes
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
   const int kbase = rank * p.ks;
 
   // Weight rows of this tile (byte bounds below 2^31, checked on the host).
-  const uint32_t wrow_bytes = MX ? (uint32_t)(K / 2) : (uint32_t)K * 2u;
+  const uint32_t wrow_bytes = row_bytes(WF, (uint32_t)K);
   const rsrc_t wr = make_rsrc(static_cast<const uint8_t*>(p.w) + (size_t)n0 * wrow_bytes,
                               TILE_N * wrow_bytes);
   const rsrc_t sr = MX ? make_rsrc(p.wscale + (size_t)n0 * (K / 32), TILE_N * (uint32_t)(K / 32))
@@ -115,10 +117,8 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
   // Byte offset, within a weight row, of this lane's first piece of a step
   // starting at K element kel: bf16 piece c covers K elements
   // kel + 32c + 8g .. +7 (one load instruction reads 64 contiguous bytes of
-  // each row); an MXFP4 lane covers kel + 32g .. +31.
-  auto w_lane_off = [&](int kel) -> uint32_t {
-    return MX ? (uint32_t)(kel / 2 + 16 * g) : (uint32_t)(kel * 2 + 16 * g);
-  };
+  // each row); a block-scaled lane covers kel + LK*g .. +LK-1.
+  auto w_lane_off = [&](int kel) -> uint32_t { return elem_byte(WF, (uint32_t)kel) + 16u * g; };
 
   f32x4 acc[RG][NT];
 #pragma unroll
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
       for (int rg = 0; rg < RG; ++rg) {
 #pragma unroll
         for (int l = 0; l < LOADS; ++l) ring[slot_s][rg][l] = ld16_if(ok, wr, row_off[rg] + lo + 64 * l);
-        if constexpr (MX) sring[slot_s][rg] = ld1_if(ok, sr, srow_off[rg] + kel / 32 + g);
+        if constexpr (MX) sring[slot_s][rg] = ld1_if(ok, sr, srow_off[rg] + (kel + LK * g) / 32);
       }
     };
 
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
             const int k = (pc / T) * 8;
             int j, s, gg;
             if constexpr (MX) {
-              j = k / 128; gg = (k % 128) / 32; s = (k % 32) / 8;
+              j = k / STEP_K; gg = (k % STEP_K) / LK; s = (k % LK) / 8;
             } else {
               j = k / (32 * C); s = (k % (32 * C)) / 32; gg = (k % 32) / 8;
             }
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
         for (int rg = 0; rg < RG; ++rg) {
           bf16x8 af;
           if constexpr (MX) {
-            af = fp4x8_bf16(a[rg][0][s], e8m0_f32(sc[rg]));
+            af = decode_operand<WF>(a[rg][0], s, e8m0_f32(sc[rg]));
           } else {
             af = as_bf16x8(a[rg][s]);
           }
@@ -361,15 +361,17 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
 // ring. At the end each wave takes every WK-th tile: one vector atomic bumps
 // all their counters (a lane per tile) and the tiles it arrived last on are
 // finished two at a time, all partial loads in flight before the sums.
-template <int NT, int WK, int WN, int D, int C, bool EPI, bool MX>
+template <int NT, int WK, int WN, int D, int C, bool EPI, int WF>
 __global__ __launch_bounds__(64 * WK * WN)
 __attribute__((amdgpu_waves_per_eu(stream_waves_per_eu(NT, WK * WN))))
 void splitk_stream_kernel(GemmParams p) {
   select_problem(p);
+  constexpr bool MX = WF != kBf16;  // block-scaled weights
+  constexpr int LK = lane_k(WF);     // K elements of one lane's 16-byte piece
   constexpr int THREADS = 64 * WK * WN;
   constexpr int LOADS = MX ? 1 : C;
-  constexpr int SUBS = MX ? 4 : C;
-  constexpr int STEP_K = MX ? 128 : 32 * C;
+  constexpr int SUBS = MX ? LK / 8 : C;
+  constexpr int STEP_K = MX ? 4 * LK : 32 * C;
   constexpr int XBATCH = 4;
   constexpr int SWK = EPI ? WK - 1 : WK;   // streaming waves per tile
   constexpr int PARKED = EPI ? SWK : WK - 1;  // partial sums parked in LDS per tile
@@ -407,7 +409,7 @@ void splitk_stream_kernel(GemmParams p) {
   const int n_i = epi_wave ? 0 : (cs - sw + SWK - 1) / SWK;  // this wave's steps per tile
   const int total = ntl * n_i;
 
-  const uint32_t wrow_bytes = MX ? (uint32_t)(K / 2) : (uint32_t)K * 2u;
+  const uint32_t wrow_bytes = row_bytes(WF, (uint32_t)K);
   const rsrc_t wr = make_rsrc(p.w, (uint32_t)N * wrow_bytes);
   const rsrc_t sr = MX ? make_rsrc(p.wscale, (uint32_t)N * (uint32_t)(K / 32)) : wr;
   const rsrc_t xr = make_rsrc(p.x, (uint32_t)T * (uint32_t)K * 2u);
@@ -430,10 +432,10 @@ void splitk_stream_kernel(GemmParams p) {
   auto issue = [&](int slot) {
     const bool ok = issued < total;
     const int kel = kbase + (sw + SWK * pf_i) * STEP_K;
-    const uint32_t lo = MX ? (uint32_t)(kel / 2 + 16 * g) : (uint32_t)(kel * 2 + 16 * g);
+    const uint32_t lo = elem_byte(WF, (uint32_t)kel) + 16u * g;
 #pragma unroll
     for (int l = 0; l < LOADS; ++l) ring[slot][l] = ld16_if(ok, wr, pf_row + lo + 64 * l);
-    if constexpr (MX) sring[slot] = ld1_if(ok, sr, pf_srow + (uint32_t)(kel / 32 + g));
+    if constexpr (MX) sring[slot] = ld1_if(ok, sr, pf_srow + (uint32_t)((kel + LK * g) / 32));
     ++issued;
     if (++pf_i == n_i) {
       pf_i = 0;
@@ -476,7 +478,7 @@ void splitk_stream_kernel(GemmParams p) {
         const int k = (q / T) * 8;
         int j, s2, gg;
         if constexpr (MX) {
-          j = k / 128; gg = (k % 128) / 32; s2 = (k % 32) / 8;
+          j = k / STEP_K; gg = (k % STEP_K) / LK; s2 = (k % LK) / 8;
         } else {
           j = k / (32 * C); s2 = (k % (32 * C)) / 32; gg = (k % 32) / 8;
         }
@@ -614,7 +616,7 @@ void splitk_stream_kernel(GemmParams p) {
       }
       bf16x8 af;
       if constexpr (MX) {
-        af = fp4x8_bf16(a[0][s2], e8m0_f32(sc));
+        af = decode_operand<WF>(a[0], s2, e8m0_f32(sc));
       } else {
         af = as_bf16x8(a[s2]);
       }
@@ -823,7 +825,7 @@ namespace {
 struct Shape {
   int rg, wk, wn, d, c;
   int max_nt;     // largest token-tile count this shape is built for (bf16)
-  int max_nt_mx;  // the same for MXFP4 weights (their decode needs registers)
+  int max_nt_mx;  // the same for block-scaled weights (their decode needs registers)
 };
 
 // The instantiated workgroup shapes (each for NT = 1..8 and both weight
@@ -843,44 +845,44 @@ constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 constexpr int kMaxXLds = 128 * 1024;  // LDS for the staged X slice (or chunk)
 constexpr int kMaxLds = 159 * 1024;   // dynamic LDS per workgroup (160 KiB per CU on gfx950)
 
-template <int NT, int SH, bool MX>
+template <int NT, int SH, int WF>
 hipError_t launch_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
   constexpr Shape sh = kShapes[SH];
-  if constexpr (NT > (MX ? sh.max_nt_mx : sh.max_nt)) {
+  if constexpr (NT > (WF != kBf16 ? sh.max_nt_mx : sh.max_nt)) {
     return hipErrorInvalidValue;  // not built: pick_tactic never selects it
   } else {
-    auto kern = splitk_gemm_kernel<NT, sh.rg, sh.wk, sh.wn, sh.d, sh.c, MX>;
+    auto kern = splitk_gemm_kernel<NT, sh.rg, sh.wk, sh.wn, sh.d, sh.c, WF>;
     hipLaunchKernelGGL(kern, dim3(t.grid, p.L), dim3(t.threads), t.lds, s, p);
     return hipGetLastError();
   }
 }
 
-template <int NT, bool MX>
+template <int NT, int WF>
 hipError_t launch_nt(int sh, const Tactic& t, const GemmParams& p, hipStream_t s) {
   switch (sh) {
-    case 0: return launch_one<NT, 0, MX>(t, p, s);
-    case 1: return launch_one<NT, 1, MX>(t, p, s);
-    case 2: return launch_one<NT, 2, MX>(t, p, s);
-    case 3: return launch_one<NT, 3, MX>(t, p, s);
-    case 4: return launch_one<NT, 4, MX>(t, p, s);
-    case 5: return launch_one<NT, 5, MX>(t, p, s);
-    case 6: return launch_one<NT, 6, MX>(t, p, s);
-    case 7: return launch_one<NT, 7, MX>(t, p, s);
+    case 0: return launch_one<NT, 0, WF>(t, p, s);
+    case 1: return launch_one<NT, 1, WF>(t, p, s);
+    case 2: return launch_one<NT, 2, WF>(t, p, s);
+    case 3: return launch_one<NT, 3, WF>(t, p, s);
+    case 4: return launch_one<NT, 4, WF>(t, p, s);
+    case 5: return launch_one<NT, 5, WF>(t, p, s);
+    case 6: return launch_one<NT, 6, WF>(t, p, s);
+    case 7: return launch_one<NT, 7, WF>(t, p, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <bool MX>
+template <int WF>
 hipError_t launch_fmt(int sh, const Tactic& t, const GemmParams& p, hipStream_t s) {
   switch (t.nt) {
-    case 1: return launch_nt<1, MX>(sh, t, p, s);
-    case 2: return launch_nt<2, MX>(sh, t, p, s);
-    case 3: return launch_nt<3, MX>(sh, t, p, s);
-    case 4: return launch_nt<4, MX>(sh, t, p, s);
-    case 5: return launch_nt<5, MX>(sh, t, p, s);
-    case 6: return launch_nt<6, MX>(sh, t, p, s);
-    case 7: return launch_nt<7, MX>(sh, t, p, s);
-    case 8: return launch_nt<8, MX>(sh, t, p, s);
+    case 1: return launch_nt<1, WF>(sh, t, p, s);
+    case 2: return launch_nt<2, WF>(sh, t, p, s);
+    case 3: return launch_nt<3, WF>(sh, t, p, s);
+    case 4: return launch_nt<4, WF>(sh, t, p, s);
+    case 5: return launch_nt<5, WF>(sh, t, p, s);
+    case 6: return launch_nt<6, WF>(sh, t, p, s);
+    case 7: return launch_nt<7, WF>(sh, t, p, s);
+    case 8: return launch_nt<8, WF>(sh, t, p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -908,12 +910,13 @@ int pick_kc(int ks, int step, int T) {
 }
 
 // Fills the launch geometry of shape `si`; false if it does not fit.
-bool shape_fits(int si, int T, int N, int ks, int S, bool mx, Tactic* t) {
+bool shape_fits(int si, int T, int N, int ks, int S, int wf, Tactic* t) {
+  const bool mx = wf != kBf16;
   const Shape& c = kShapes[si];
   if (t->nt > (mx ? c.max_nt_mx : c.max_nt)) return false;
   const int tile_n = 16 * c.rg * c.wn;
   if (N % tile_n) return false;
-  const int step = mx ? 128 : 32 * c.c;
+  const int step = mx ? 4 * lane_k(wf) : 32 * c.c;
   const int kc = pick_kc(ks, step, T);
   if (kc < 0) return false;
   const int x_lds = T * kc * 2;
@@ -956,32 +959,32 @@ constexpr int kStreamMaxX = 128 * 1024;
 constexpr int kClusterMaxGrid = 512;
 constexpr long kClusterMaxBatchGrid = 8192;
 
-template <int NT, int SH, bool MX>
+template <int NT, int SH, int WF>
 hipError_t launch_stream_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
   constexpr StreamShape sh = kStreamShapes[SH];
-  auto kern = splitk_stream_kernel<NT, sh.wk, sh.wn, sh.d, sh.c, sh.epi != 0, MX>;
+  auto kern = splitk_stream_kernel<NT, sh.wk, sh.wn, sh.d, sh.c, sh.epi != 0, WF>;
   hipLaunchKernelGGL(kern, dim3(t.grid, p.L), dim3(t.threads), t.lds, s, p);
   return hipGetLastError();
 }
 
-template <int NT, bool MX>
+template <int NT, int WF>
 hipError_t launch_stream_nt(int sh, const Tactic& t, const GemmParams& p, hipStream_t s) {
   switch (sh) {
-    case 0: return launch_stream_one<NT, 0, MX>(t, p, s);
-    case 1: return launch_stream_one<NT, 1, MX>(t, p, s);
-    case 2: return launch_stream_one<NT, 2, MX>(t, p, s);
-    case 3: return launch_stream_one<NT, 3, MX>(t, p, s);
-    case 4: return launch_stream_one<NT, 4, MX>(t, p, s);
-    case 5: return launch_stream_one<NT, 5, MX>(t, p, s);
+    case 0: return launch_stream_one<NT, 0, WF>(t, p, s);
+    case 1: return launch_stream_one<NT, 1, WF>(t, p, s);
+    case 2: return launch_stream_one<NT, 2, WF>(t, p, s);
+    case 3: return launch_stream_one<NT, 3, WF>(t, p, s);
+    case 4: return launch_stream_one<NT, 4, WF>(t, p, s);
+    case 5: return launch_stream_one<NT, 5, WF>(t, p, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <bool MX>
+template <int WF>
 hipError_t launch_stream_fmt(int sh, const Tactic& t, const GemmParams& p, hipStream_t s) {
   switch (t.nt) {
-    case 1: return launch_stream_nt<1, MX>(sh, t, p, s);
-    case 2: return launch_stream_nt<2, MX>(sh, t, p, s);
+    case 1: return launch_stream_nt<1, WF>(sh, t, p, s);
+    case 2: return launch_stream_nt<2, WF>(sh, t, p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -992,10 +995,10 @@ int env_int(const char* name, int dflt) {
 }
 
 // Fills the geometry of persistent shape `si`; false if it does not apply.
-bool stream_fits(int si, int T, int N, int ks, int S, bool mx, Tactic* t, int L = 1) {
+bool stream_fits(int si, int T, int N, int ks, int S, int wf, Tactic* t, int L = 1) {
   const StreamShape& c = kStreamShapes[si];
   if (t->nt > kStreamMaxNT || ks == 0) return false;
-  const int step = mx ? 128 : 32 * c.c;
+  const int step = wf != kBf16 ? 4 * lane_k(wf) : 32 * c.c;
   if (ks % step) return false;
   const int cs = ks / step;
   const int streaming = c.epi ? c.wk - 1 : c.wk;
@@ -1034,12 +1037,13 @@ bool stream_fits(int si, int T, int N, int ks, int S, bool mx, Tactic* t, int L 
   return true;
 }
 
-bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L) {
+bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L) {
+  const bool mx = wf != kBf16;
   Tactic t{};
   t.nt = (T + 15) / 16;
   if (t.nt < 1) t.nt = 1;
   if (t.nt > 8) return false;
-  t.mx = mx ? 1 : 0;
+  t.wf = wf;
   const int ks = K / S;
   const int tr = T > 0 ? T : 1;
 
@@ -1049,7 +1053,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L) {
   const int kind = env_int("SKGEMM_KIND", -1);
   if (kind == 2 || kind < 0) {
     Tactic c = t;
-    if (cluster_fits(tr, N, ks, S, mx, env_int("SKGEMM_FOLD", 8), env_int("SKGEMM_CLUSTER_C", 0), &c)) {
+    if (cluster_fits(tr, N, ks, S, wf, env_int("SKGEMM_FOLD", 8), env_int("SKGEMM_CLUSTER_C", 0), &c)) {
       // Whole tiles per workgroup pay off while the grid is about one
       // workgroup per CU; beyond, the persistent kernel's staged activations
       // and amortised ramp-up win. Every cluster workgroup re-reads all of X
@@ -1057,7 +1061,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L) {
       // batch the cluster kernel stays only while that is small (measured:
       // T=1 K=1024 N=1024 batches run 1.1 vs 1.6 us a problem on it, the
       // T=8 K=7168 N=2048 ones 9.6 vs 6.4 us on the persistent kernel).
-      const double x_per_w = (double)tr * 2.0 / ((double)c.tile_n * (mx ? 0.53125 : 2.0));
+      const double x_per_w = (double)tr * 2.0 / ((double)c.tile_n * weight_bytes_per_elem(wf));
       const bool small = L == 1 ? c.grid <= kClusterMaxGrid
                                 : (x_per_w <= 0.5 && (long)c.grid * L <= kClusterMaxBatchGrid);
       if (kind == 2 || small) {
@@ -1071,7 +1075,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L) {
   // SKGEMM_STREAM=<index> forces one of its shapes, for tuning runs).
   if (kind == 1 || kind < 0) {
     const int forced = env_int("SKGEMM_STREAM", -2);
-    if (forced >= 0 && forced < kNumStreamShapes && stream_fits(forced, tr, N, ks, S, mx, &t, L)) {
+    if (forced >= 0 && forced < kNumStreamShapes && stream_fits(forced, tr, N, ks, S, wf, &t, L)) {
       *out = t;
       return true;
     }
@@ -1087,7 +1091,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L) {
       const int* pref = many;
       for (int si : many) {
         Tactic probe = t;
-        if (stream_fits(si, tr, N, ks, S, mx, &probe, L)) {
+        if (stream_fits(si, tr, N, ks, S, wf, &probe, L)) {
           const int groups = probe.grid / S;
           const int per_wg = (N / 16 + groups - 1) / groups;
           if (per_wg <= 4) pref = few;
@@ -1096,7 +1100,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L) {
       }
       for (int oi = 0; oi < kNumStreamShapes; ++oi) {
         const int si = pref[oi];
-        if (stream_fits(si, tr, N, ks, S, mx, &t, L)) {
+        if (stream_fits(si, tr, N, ks, S, wf, &t, L)) {
           *out = t;
           return true;
         }
@@ -1106,7 +1110,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L) {
   if (kind == 1) return false;
   // Many tokens: the wide-tile kernel with double-buffered X chunks.
   if (kind == 3 || kind < 0) {
-    if (wide_fits(tr, N, ks, S, mx, &t)) {
+    if (wide_fits(tr, N, ks, S, wf, &t)) {
       *out = t;
       return true;
     }
@@ -1115,7 +1119,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L) {
   // A tiled shape forced for tuning runs (SKGEMM_SHAPE=<index>), if it fits.
   if (const char* e = getenv("SKGEMM_SHAPE")) {
     const int si = atoi(e);
-    if (si >= 0 && si < kNumShapes && shape_fits(si, tr, N, ks, S, mx, &t)) {
+    if (si >= 0 && si < kNumShapes && shape_fits(si, tr, N, ks, S, wf, &t)) {
       *out = t;
       return true;
     }
@@ -1130,7 +1134,7 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L) {
                 "every shape appears in both orders");
   const int* order = (t.nt <= 2) ? small_t : large_t;
   for (int oi = 0; oi < kNumShapes; ++oi) {
-    if (shape_fits(order[oi], tr, N, ks, S, mx, &t)) {
+    if (shape_fits(order[oi], tr, N, ks, S, wf, &t)) {
       *out = t;
       return true;
     }
@@ -1141,11 +1145,22 @@ bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L) {
 hipError_t launch_gemm(const Tactic& t, const GemmParams& p, hipStream_t s) {
   if (t.kind == 3) return launch_wide(t, p, s);
   if (t.kind == 2) return launch_cluster(t, p, s);
-  if (t.kind == 1) return t.mx ? launch_stream_fmt<true>(t.shape, t, p, s)
-                               : launch_stream_fmt<false>(t.shape, t, p, s);
+  if (t.kind == 1) {
+    switch (t.wf) {
+      case kBf16: return launch_stream_fmt<kBf16>(t.shape, t, p, s);
+      case kMxfp4: return launch_stream_fmt<kMxfp4>(t.shape, t, p, s);
+      case kMxfp8: return launch_stream_fmt<kMxfp8>(t.shape, t, p, s);
+    }
+    return hipErrorInvalidValue;
+  }
   const int sh = shape_index(t);
   if (sh < 0) return hipErrorInvalidValue;
-  return t.mx ? launch_fmt<true>(sh, t, p, s) : launch_fmt<false>(sh, t, p, s);
+  switch (t.wf) {
+    case kBf16: return launch_fmt<kBf16>(sh, t, p, s);
+    case kMxfp4: return launch_fmt<kMxfp4>(sh, t, p, s);
+    case kMxfp8: return launch_fmt<kMxfp8>(sh, t, p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace skg

@@ -3,6 +3,7 @@
 // run the same inline helpers the GEMM kernels use.
 
 #include "device/mxfp4.h"
+#include "device/wfmt.h"
 #include "device/pack.h"
 #include "device/types.h"
 #include "device/wave.h"
@@ -53,6 +54,22 @@ __global__ __launch_bounds__(kThreads) void mxfp4_dequant_kernel(const uint32_t*
   const size_t col = i % dwords_per_row;  // elements 8 col .. 8 col + 7
   const uint32_t code = ws[row * (K / 32) + col / 4];
   const bf16x8 v = fp4x8_bf16(wq[i], e8m0_f32(code));
+  out[i] = __builtin_bit_cast(u32x4, v);
+}
+
+// One thread per pair of dwords (8 E4M3 codes): W_out[n, 8i .. 8i+7] =
+// decode(codes, scale of their 32-element block).
+__global__ __launch_bounds__(kThreads) void mxfp8_dequant_kernel(const u32x2* wq,
+                                                                 const uint8_t* ws, u32x4* out,
+                                                                 int N, int K) {
+  const size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t groups_per_row = (size_t)K / 8;
+  if (i >= (size_t)N * groups_per_row) return;
+  const size_t row = i / groups_per_row;
+  const size_t col = i % groups_per_row;  // elements 8 col .. 8 col + 7
+  const uint32_t code = ws[row * (K / 32) + col / 4];
+  const u32x2 w = wq[i];
+  const bf16x8 v = fp8x8_bf16(w.x, w.y, e8m0_f32(code));
   out[i] = __builtin_bit_cast(u32x4, v);
 }
 
@@ -118,6 +135,16 @@ hipError_t launch_mxfp4_dequant(const void* wq, const void* ws, void* out, int N
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(mxfp4_dequant_kernel, dim3(blocks_for(n, kThreads)), dim3(kThreads), 0, s,
                      static_cast<const uint32_t*>(wq), static_cast<const uint8_t*>(ws),
+                     static_cast<u32x4*>(out), N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp8_dequant(const void* wq, const void* ws, void* out, int N, int K,
+                                hipStream_t s) {
+  const size_t n = (size_t)N * (size_t)(K / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(mxfp8_dequant_kernel, dim3(blocks_for(n, kThreads)), dim3(kThreads), 0, s,
+                     static_cast<const u32x2*>(wq), static_cast<const uint8_t*>(ws),
                      static_cast<u32x4*>(out), N, K);
   return hipGetLastError();
 }

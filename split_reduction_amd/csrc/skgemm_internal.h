@@ -60,7 +60,7 @@ struct Tactic {
   int threads;  // 64 * wk * wn
   int lds;      // dynamic LDS bytes
   int grid;     // workgroups = (N / tile_n) * split_k
-  int mx;       // 1 for MXFP4 weights
+  int wf;       // weight format: 0 bf16, 1 MXFP4, 2 MXFP8 (device/wfmt.h)
   int kind;     // 0: one tile per workgroup; 1: persistent stream kernel;
                 // 2: all split ranks of a tile in one workgroup;
                 // 3: wide tiles with double-buffered X chunks (33..128 tokens)
@@ -69,20 +69,21 @@ struct Tactic {
   int resident; // workgroups per CU the grid sizing counts on (0: none assumed)
 };
 
-// Picks the configuration for a launch over T <= 128 rows; returns false if no
-// instantiated configuration fits (never for validated shapes).
-bool pick_tactic(int T, int N, int K, int S, bool mx, Tactic* out, int L = 1);
+// Picks the configuration for a launch over T <= 128 rows of weight format wf
+// (L problems per launch); returns false if no instantiated configuration
+// fits (never for validated shapes).
+bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L = 1);
 
 // Fills the configuration of the one-workgroup-per-tile kernel (kind 2) for a
 // launch over T <= 32 rows, folding at most max_fold ways (force_c > 0 pins
 // the pieces per lane for bf16); false if it does not apply.
-bool cluster_fits(int T, int N, int ks, int S, bool mx, int max_fold, int force_c, Tactic* t);
+bool cluster_fits(int T, int N, int ks, int S, int wf, int max_fold, int force_c, Tactic* t);
 hipError_t launch_cluster(const Tactic& t, const GemmParams& p, hipStream_t stream);
 
 // Fills the configuration of the wide-tile kernel (kind 3) for 33 <= T <= 128
 // rows; false if it does not apply (N % 256, K slice not a whole number of
 // X chunks).
-bool wide_fits(int T, int N, int ks, int S, bool mx, Tactic* t);
+bool wide_fits(int T, int N, int ks, int S, int wf, Tactic* t);
 hipError_t launch_wide(const Tactic& t, const GemmParams& p, hipStream_t stream);
 
 // Enqueues one launch (T <= 128). Returns the launch's hipError_t.
@@ -93,6 +94,8 @@ hipError_t launch_pack_bf16(const float* in, uint32_t* out, size_t n_pairs, hipS
 hipError_t launch_pack_e4m3(const float* in, uint32_t* out, size_t n_quads, hipStream_t s);
 hipError_t launch_wave_sum(const float* in, float* out, size_t n_waves, hipStream_t s);
 hipError_t launch_mxfp4_dequant(const void* wq, const void* ws, void* out, int N, int K,
+                                hipStream_t s);
+hipError_t launch_mxfp8_dequant(const void* wq, const void* ws, void* out, int N, int K,
                                 hipStream_t s);
 // Plain coalesced read of `bytes` (a multiple of 16) with kReadProbeBlocks
 // workgroups of 1024 lanes (two per CU); sink needs kReadProbeBlocks words.

@@ -26,9 +26,9 @@
 //    last rank to arrive finishes the column instead.
 
 #include "device/mfma.h"
-#include "device/mxfp4.h"
 #include "device/pack.h"
 #include "device/types.h"
+#include "device/wfmt.h"
 #include "skgemm_internal.h"
 
 namespace skg {
@@ -41,13 +41,15 @@ constexpr int wide_kc(int nt) { return nt <= 4 ? 512 : 256; }  // K elements per
 
 }  // namespace
 
-template <int NT, bool MX>
+template <int NT, int WF>
 __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams p) {
   select_problem(p);
+  constexpr bool MX = WF != kBf16;            // block-scaled weights
+  constexpr int LK = lane_k(WF);              // K elements of one lane's 16-byte piece
   constexpr int RG = 2;                       // 16-row groups per wave
   constexpr int THREADS = 64 * kWideWaves;
-  constexpr int SUBS = MX ? 4 : 1;            // MFMA K-steps per load step
-  constexpr int STEP_K = MX ? 128 : 32;       // K elements of one load step
+  constexpr int SUBS = MX ? LK / 8 : 1;       // MFMA K-steps per load step
+  constexpr int STEP_K = MX ? 4 * LK : 32;    // K elements of one load step
   constexpr int KC = wide_kc(NT);
   constexpr int CS = KC / STEP_K;             // load steps per chunk
   // Ring depth in load steps (divides CS): 8 steps = 16 KiB of weights in
@@ -76,7 +78,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
   const int nchunks = p.ks / KC;
   const int total = nchunks * CS;  // load steps of this wave
 
-  const uint32_t wrow_bytes = MX ? (uint32_t)(K / 2) : (uint32_t)K * 2u;
+  const uint32_t wrow_bytes = row_bytes(WF, (uint32_t)K);
   const rsrc_t wr = make_rsrc(static_cast<const uint8_t*>(p.w) + (size_t)n0 * wrow_bytes,
                               (uint32_t)kWideRows * wrow_bytes);
   const rsrc_t sr = MX ? make_rsrc(p.wscale + (size_t)n0 * (K / 32), (uint32_t)kWideRows * (uint32_t)(K / 32))
@@ -97,11 +99,11 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
   auto issue = [&](int slot, int q) {
     const bool ok = q < total;
     const int kel = kbase + q * STEP_K;
-    const uint32_t lo = MX ? (uint32_t)(kel / 2 + 16 * g) : (uint32_t)(kel * 2 + 16 * g);
+    const uint32_t lo = elem_byte(WF, (uint32_t)kel) + 16u * g;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
       ring[slot][rg] = ld16_if(ok, wr, row_off[rg] + lo);
-      if constexpr (MX) sring[slot][rg] = ld1_if(ok, sr, srow_off[rg] + (uint32_t)(kel / 32 + g));
+      if constexpr (MX) sring[slot][rg] = ld1_if(ok, sr, srow_off[rg] + (uint32_t)((kel + LK * g) / 32));
     }
   };
 
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
         const int k = (pc / TP) * 8;
         int j, s2, gg;
         if constexpr (MX) {
-          j = k / 128; gg = (k % 128) / 32; s2 = (k % 32) / 8;
+          j = k / STEP_K; gg = (k % STEP_K) / LK; s2 = (k % LK) / 8;
         } else {
           j = k / 32; s2 = 0; gg = (k % 32) / 8;
         }
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
       for (int rg = 0; rg < RG; ++rg) {
         bf16x8 af;
         if constexpr (MX) {
-          af = fp4x8_bf16(ring[slot][rg][s2], e8m0_f32(sring[slot][rg]));
+          af = decode_operand<WF>(ring[slot][rg], s2, e8m0_f32(sring[slot][rg]));
         } else {
           af = as_bf16x8(ring[slot][rg]);
         }
@@ -336,28 +338,29 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
 
 namespace {
 
-template <int NT, bool MX>
+template <int NT, int WF>
 hipError_t launch_wide_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((splitk_wide_kernel<NT, MX>), dim3(t.grid, p.L), dim3(t.threads), t.lds, s, p);
+  hipLaunchKernelGGL((splitk_wide_kernel<NT, WF>), dim3(t.grid, p.L), dim3(t.threads), t.lds, s, p);
   return hipGetLastError();
 }
 
-template <bool MX>
+template <int WF>
 hipError_t launch_wide_fmt(const Tactic& t, const GemmParams& p, hipStream_t s) {
   switch (t.nt) {
-    case 3: return launch_wide_one<3, MX>(t, p, s);
-    case 4: return launch_wide_one<4, MX>(t, p, s);
-    case 5: return launch_wide_one<5, MX>(t, p, s);
-    case 6: return launch_wide_one<6, MX>(t, p, s);
-    case 7: return launch_wide_one<7, MX>(t, p, s);
-    case 8: return launch_wide_one<8, MX>(t, p, s);
+    case 3: return launch_wide_one<3, WF>(t, p, s);
+    case 4: return launch_wide_one<4, WF>(t, p, s);
+    case 5: return launch_wide_one<5, WF>(t, p, s);
+    case 6: return launch_wide_one<6, WF>(t, p, s);
+    case 7: return launch_wide_one<7, WF>(t, p, s);
+    case 8: return launch_wide_one<8, WF>(t, p, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool wide_fits(int T, int N, int ks, int S, bool mx, Tactic* t) {
+bool wide_fits(int T, int N, int ks, int S, int wf, Tactic* t) {
+  const bool mx = wf != kBf16;
   const int nt = (T + 15) / 16;
   if (nt < 3 || nt > 8 || N % kWideRows || ks <= 0) return false;
   const int kc = wide_kc(nt);
@@ -383,7 +386,12 @@ bool wide_fits(int T, int N, int ks, int S, bool mx, Tactic* t) {
 }
 
 hipError_t launch_wide(const Tactic& t, const GemmParams& p, hipStream_t s) {
-  return t.mx ? launch_wide_fmt<true>(t, p, s) : launch_wide_fmt<false>(t, p, s);
+  switch (t.wf) {
+    case kBf16: return launch_wide_fmt<kBf16>(t, p, s);
+    case kMxfp4: return launch_wide_fmt<kMxfp4>(t, p, s);
+    case kMxfp8: return launch_wide_fmt<kMxfp8>(t, p, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace skg

@@ -82,3 +82,17 @@ def assert_parity(c_bits, c_ref, K, what, rms=None):
     log(f"  {what}: max |err|/bound = {ratio:.4f}")
     assert ratio <= 1.0, f"{what}: parity ratio {ratio}"
     return ratio
+
+
+def run_mxfp8(x_bits, wq8, ws, split_k):
+    import split_reduction_amd as sk
+
+    T, K = x_bits.shape
+    N = wq8.shape[0]
+    X = to_dev_bf16(x_bits)
+    Wq = to_dev_u8(wq8)
+    Ws = to_dev_u8(ws)
+    C = empty_bf16(T, N)
+    sk.skgemm_mxfp8(Wq, Ws, X, C, T, N, K, split_k)
+    torch().cuda.synchronize()
+    return bf16_bits(C)

@@ -13,7 +13,7 @@ import split_reduction_amd as sk
 from oracle import formats as F
 from oracle import gemm as G
 from tests.gpu_util import (DEV, assert_parity, bf16_bits, empty_bf16, log, run_bf16, run_mxfp4,
-                            to_dev_bf16, to_dev_u8, torch)
+                            run_mxfp8, to_dev_bf16, to_dev_u8, torch)
 import workloads
 
 pytestmark = pytest.mark.gpu
@@ -182,6 +182,58 @@ def test_mxfp4_integer_operands_bit_exact(S):
     assert np.array_equal(c, F.f32_to_bf16_rne(exact.astype(np.float32)))
 
 
+MX8_CASES = [
+    (1, 256, 512, 1),
+    (3, 4096, 512, 4),
+    (16, 1024, 1024, 2),
+    (40, 2048, 1024, 4),
+    (128, 512, 2048, 2),
+    (130, 64, 256, 1),
+]
+
+
+@pytest.mark.parametrize("T,N,K,S", MX8_CASES)
+def test_mxfp8_parity_small(T, N, K, S):
+    log(f"mxfp8 parity T={T} N={N} K={K} S={S} tactic={sk.skgemm_tactic_for(T, N, K, S, 2)}")
+    x, wq8, ws = workloads.small_mxfp8_case(T, K, N, seed=3500 + T + N + K + S)
+    assert_parity(run_mxfp8(x, wq8, ws, S), G.gemm_mxfp8_ref(x, wq8, ws), K, f"mxfp8 T={T} N={N} K={K} S={S}")
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_mxfp8_integer_operands_bit_exact(S):
+    T, N, K = 20, 256, 1024
+    log(f"mxfp8 integer exact S={S}")
+    rng = np.random.default_rng(60 + S)
+    x = workloads.to_bf16_bits(rng.integers(-3, 4, size=(T, K)).astype(np.float32))
+    ints = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0, 0xC4, 0x80], dtype=np.uint8)  # 0 +-1..4, -0
+    wq8 = rng.choice(ints, size=(N, K))
+    ws = np.full((N, K // 32), 127, dtype=np.uint8)
+    exact = G.gemm_mxfp8_ref(x, wq8, ws)
+    c = run_mxfp8(x, wq8, ws, S)
+    assert np.array_equal(F.bf16_bits_to_f64(c), F.bf16_bits_to_f64(F.f32_to_bf16_rne(exact.astype(np.float32))))
+
+
+def test_mxfp8_batched_and_workload():
+    t = torch()
+    T, N, K, S, L = 16, 512, 2048, 4, 3
+    cases = [workloads.small_mxfp8_case(T, K, N, seed=9600 + l) for l in range(L)]
+    log(f"batched mxfp8 L={L} T={T} N={N} K={K} S={S}")
+    Wq = to_dev_u8(np.stack([c[1] for c in cases]))
+    Ws = to_dev_u8(np.stack([c[2] for c in cases]))
+    X = to_dev_bf16(np.stack([c[0] for c in cases]))
+    C = t.empty((L, T, N), dtype=t.bfloat16, device=DEV)
+    sk.skgemm_mxfp8_batched(Wq, Ws, X, C, T, N, K, S, L, N * K, N * K // 32, T * K * 2, T * N * 2)
+    t.cuda.synchronize()
+    cb = bf16_bits(C)
+    for l, (x, wq8, ws) in enumerate(cases):
+        assert_parity(cb[l], G.gemm_mxfp8_ref(x, wq8, ws), K, f"mxfp8 batch {l}")
+    w = workloads.WORKLOADS["mxfp8_t16_k7168_n4096"]
+    log(f"workload {w.name} tactic={sk.skgemm_tactic_for(w.T, w.N, w.K, w.split_k, 2)}")
+    x = workloads.gen_x(w)
+    wq8, ws = workloads.gen_w_mxfp8(w)
+    assert_parity(run_mxfp8(x, wq8, ws, w.split_k), G.gemm_mxfp8_ref(x, wq8, ws), w.K, w.name)
+
+
 # ------------------------------------------------------ full workloads -----
 
 
@@ -302,6 +354,18 @@ def test_every_kernel_shape(env, monkeypatch):
         x, wq, ws = workloads.small_mxfp4_case(T, K, N, seed=6000 + T + S)
         assert_parity(run_mxfp4(x, wq, ws, S), G.gemm_mxfp4_ref(x, wq, ws), K, f"{env} mx T={T}")
         ran += 1
+    for (T, N, K, S) in [(5, 512, 1024, 4), (30, 256, 512, 2), (1, 128, 1024, 2), (5, 512, 4096, 2),
+                         (20, 256, 1024, 1)]:
+        try:
+            tac = sk.skgemm_tactic_for(T, N, K, S, 2)
+        except sk.SkgemmError as e:
+            assert e.code == sk.SKGEMM_ESHAPE
+            continue
+        log(f"forced {env}: mxfp8 T={T} N={N} K={K} S={S} tactic={tac}")
+        assert tac["kind"] == kind
+        x, wq8, ws = workloads.small_mxfp8_case(T, K, N, seed=6100 + T + S)
+        assert_parity(run_mxfp8(x, wq8, ws, S), G.gemm_mxfp8_ref(x, wq8, ws), K, f"{env} mx8 T={T}")
+        ran += 1
     assert ran >= 4
 
 
@@ -373,6 +437,12 @@ def test_wide_kernel(wait, monkeypatch):
         assert tac["kind"] == "wide"
         x, wq, ws = workloads.small_mxfp4_case(T, K, N, seed=9100 + T + S)
         assert_parity(run_mxfp4(x, wq, ws, S), G.gemm_mxfp4_ref(x, wq, ws), K, f"wide mx T={T} S={S}")
+    for (T, N, K, S) in WIDE_MX_CASES:
+        tac = sk.skgemm_tactic_for(T, N, K, S, 2)
+        log(f"wide wait={wait}: mxfp8 T={T} N={N} K={K} S={S} tactic={tac}")
+        assert tac["kind"] == "wide"
+        x, wq8, ws = workloads.small_mxfp8_case(T, K, N, seed=9150 + T + S)
+        assert_parity(run_mxfp8(x, wq8, ws, S), G.gemm_mxfp8_ref(x, wq8, ws), K, f"wide mx8 T={T} S={S}")
 
 
 @pytest.mark.parametrize("S", [1, 2, 4, 8])

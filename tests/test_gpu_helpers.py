@@ -124,3 +124,36 @@ def test_read_probe_reads_and_writes_nothing():
     with pytest.raises(sk.SkgemmError) as e:
         sk.skgemm_read_probe(buf, 24, sink)
     assert e.value.code == sk.SKGEMM_EINVAL
+
+
+def test_mxfp8_dequant_every_code_and_scale():
+    """The in-register E4M3 decode, bit for bit against the oracle: every
+    code (NaN codes stay NaN) at every scale 10..246, and the byte order
+    (element k of a row in byte k)."""
+    t = torch()
+    codes = np.arange(256, dtype=np.uint8)
+    scales = np.arange(10, 247, dtype=np.uint8)
+    n = len(scales)
+    wq8 = np.tile(codes, (n, 1))
+    ws = np.repeat(scales.reshape(n, 1), 256 // 32, axis=1)
+    out = t.empty((n, 256), dtype=t.int16, device=DEV)
+    log(f"mxfp8 dequant {n} scales x 256 codes")
+    sk.skgemm_mxfp8_dequant(to_dev_u8(wq8), to_dev_u8(ws), out, n, 256)
+    t.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    want = F.mxfp8_dequant_bf16_bits(wq8, ws)
+    nan_g = np.isnan(F.bf16_bits_to_f64(got))
+    nan_w = np.isnan(F.bf16_bits_to_f64(want))
+    assert np.array_equal(nan_g, nan_w)
+    assert np.array_equal(got[~nan_w], want[~nan_w])
+
+
+def test_mxfp8_dequant_workload_tensor():
+    w = workloads.WORKLOADS["mxfp8_t16_k7168_n4096"]
+    wq8, ws = workloads.gen_w_mxfp8(w)
+    t = torch()
+    out = t.empty((w.N, w.K), dtype=t.int16, device=DEV)
+    log("mxfp8 dequant of the whole T=16 K=7168 N=4096 weight tensor")
+    sk.skgemm_mxfp8_dequant(to_dev_u8(wq8), to_dev_u8(ws), out, w.N, w.K)
+    t.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint16), F.mxfp8_dequant_bf16_bits(wq8, ws))

@@ -19,6 +19,8 @@ bf16_t32_k7168_n18432        32   7168  18432    8  as above, 1% outlier K
                                                     channels of X scaled x50
 mxfp4_t16_k7168_n4096        16   7168   4096    4  nibbles U{0..15}, scale
                                                     codes U{118..130}, X~N(0,1)
+mxfp8_t16_k7168_n4096        16   7168   4096    4  E4M3 codes U over the 254
+                                                    non-NaN bytes, scales as above
 bf16_sweep_k16384_n16384    T*  16384  16384   S*  W~N(0,0.01^2), X~N(0,1)
 =========================  ====  =====  =====  ===  ===========================
 
@@ -62,6 +64,8 @@ class Workload:
     def weight_bytes(self) -> int:
         if self.kind == "mxfp4":
             return self.N * self.K // 2 + self.N * self.K // 32
+        if self.kind == "mxfp8":
+            return self.N * self.K + self.N * self.K // 32
         return self.N * self.K * 2
 
     def flops(self) -> int:
@@ -76,6 +80,8 @@ WORKLOADS = {
         outlier_frac=0.01, outlier_scale=50.0,
     ),
     "mxfp4_t16_k7168_n4096": Workload("mxfp4_t16_k7168_n4096", "mxfp4", 16, 7168, 4096, 4, SEED_BASE + 4),
+    # the MXFP4 shape with eight-bit E4M3 elements (an extra, not one of the pages' workloads)
+    "mxfp8_t16_k7168_n4096": Workload("mxfp8_t16_k7168_n4096", "mxfp8", 16, 7168, 4096, 4, SEED_BASE + 200),
 }
 
 
@@ -147,6 +153,31 @@ def gen_w_mxfp4(w: Workload) -> tuple[np.ndarray, np.ndarray]:
     wq = rng.integers(0, 256, size=(w.N, w.K // 2), dtype=np.uint8)
     ws = rng.integers(w.scale_lo, w.scale_hi + 1, size=(w.N, w.K // 32), dtype=np.uint8)
     return wq, ws
+
+
+def mxfp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniform E4M3FN codes over the 254 non-NaN bytes (0x7F and 0xFF excluded)."""
+    c = rng.integers(0, 254, size=shape, dtype=np.int32)
+    c = c + (c >= 0x7F)  # skip 0x7F
+    c = c + (c >= 0xFF)  # skip 0xFF (0xFE + 1 above lands on 0xFF)
+    return np.minimum(c, 0xFE).astype(np.uint8)
+
+
+def gen_w_mxfp8(w: Workload) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP8 weights: (Wq8 uint8 [N, K] E4M3 codes, Wscale uint8 [N, K/32])."""
+    rng = np.random.default_rng(w.seed * 1000 + 4)
+    wq8 = mxfp8_codes(rng, (w.N, w.K))
+    ws = rng.integers(w.scale_lo, w.scale_hi + 1, size=(w.N, w.K // 32), dtype=np.uint8)
+    return wq8, ws
+
+
+def small_mxfp8_case(T: int, K: int, N: int, seed: int, lo: int = 118, hi: int = 130):
+    """A small seeded (X, Wq8, Wscale) triple for parity tests."""
+    rng = np.random.default_rng(seed)
+    x = to_bf16_bits(rng.standard_normal((T, K), dtype=np.float32))
+    wq8 = mxfp8_codes(rng, (N, K))
+    ws = rng.integers(lo, hi + 1, size=(N, K // 32), dtype=np.uint8)
+    return x, wq8, ws
 
 
 def small_bf16_case(T: int, K: int, N: int, seed: int, w_sigma: float = 0.02):
