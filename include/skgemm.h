@@ -207,6 +207,23 @@ SKGEMM_API int skgemm_pack_e4m3(const float* in, uint32_t* out, size_t n_quads, 
 SKGEMM_API int skgemm_wave_sum(const float* in, float* out, size_t n_waves, hipStream_t stream);
 
 /*
+ * skgemm_health: the bounded-wait report of (current device, stream) (page
+ * vllm.models.muse_spark.amd.mono.kernels.dev, _spin_bounded: a time-out
+ * writes a record instead of hanging). With split_k > 1 the owner rank of a
+ * tile waits a bounded time for the other ranks; when that time runs out it
+ * hands the tile to the last rank to arrive (the result is unchanged) and
+ * records it. Copies min(n_words, 128) words to host memory `words` and
+ * clears them on the device: word 0 = time-outs since the last call; words
+ * 8 + 8r .. 8 + 8r + 4 (r < min(count, 15)) = {1, the tile's first 16-row
+ * group, owner rank, problem index in a batch, ticks waited}; other words 0.
+ * A time-out means the launch's workgroups were not all resident at once
+ * (e.g. a concurrent kernel held CUs): a slow path, not a wrong result.
+ * Synchronises `stream`; SKGEMM_EINVAL under graph capture. A stream with no
+ * workspace yet reports zeros.
+ */
+SKGEMM_API int skgemm_health(uint32_t* words, size_t n_words, hipStream_t stream);
+
+/*
  * skgemm_read_probe: a reference for the weight stream, not part of the
  * method: reads `bytes` of device memory at src once, with plain coalesced
  * 16-byte loads, 512 workgroups of 1024 lanes each reading one contiguous

@@ -56,6 +56,7 @@ def _declare(lib):
         "skgemm_last_hip_error": [],
         "skgemm_set_timeline": [vp, sz],
         "skgemm_read_probe": [vp, sz, vp, st],
+        "skgemm_health": [vp, sz, st],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -214,6 +215,16 @@ def skgemm_set_timeline(buf, capacity: int) -> None:
 def skgemm_read_probe(src, nbytes: int, sink, stream=None) -> None:
     """Plain coalesced read of nbytes at src (the streaming-read reference)."""
     _check(lib().skgemm_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "skgemm_read_probe")
+
+
+def skgemm_health(stream=None) -> dict:
+    """Owner time-outs of the stream's split-K hand-off since the last call
+    (read and cleared): {"timeouts": n, "records": [(group, rank, problem, ticks), ...]}."""
+    words = (ctypes.c_uint32 * 128)()
+    _check(lib().skgemm_health(words, 128, _stream(stream)), "skgemm_health")
+    recs = [tuple(words[8 + 8 * r + i] for i in range(1, 5))
+            for r in range(min(words[0], 15)) if words[8 + 8 * r] == 1]
+    return {"timeouts": int(words[0]), "records": recs}
 
 
 def skgemm_strerror(code: int) -> str:

@@ -70,7 +70,7 @@ int check_gemm(int wf, const void* w, const void* ws, const void* x, const void*
 struct Workspace {
   float* part = nullptr;
   size_t part_bytes = 0;
-  uint32_t* cnt = nullptr;
+  uint32_t* cnt = nullptr;  // cnt_count counters, then kHealthWords health words
   size_t cnt_count = 0;
 };
 
@@ -105,11 +105,12 @@ int ensure_workspace(hipStream_t stream, size_t part_bytes, size_t cnt_count, Wo
   nw.part_bytes = std::max(part_bytes, (size_t)256);
   nw.cnt_count = std::max(cnt_count, (size_t)64);
   if (hipMalloc((void**)&nw.part, nw.part_bytes) != hipSuccess) return SKGEMM_ENOMEM;
-  if (hipMalloc((void**)&nw.cnt, nw.cnt_count * sizeof(uint32_t)) != hipSuccess) {
+  const size_t words = nw.cnt_count + skg::kHealthWords;
+  if (hipMalloc((void**)&nw.cnt, words * sizeof(uint32_t)) != hipSuccess) {
     (void)hipFree(nw.part);
     return SKGEMM_ENOMEM;
   }
-  e = hipMemsetAsync(nw.cnt, 0, nw.cnt_count * sizeof(uint32_t), stream);
+  e = hipMemsetAsync(nw.cnt, 0, words * sizeof(uint32_t), stream);
   if (e != hipSuccess) {
     (void)hipFree(nw.part);
     (void)hipFree(nw.cnt);
@@ -194,6 +195,7 @@ int run_gemm(int wf, const void* w, const void* ws, const void* x, void* c, int 
     const bool all_resident =
         tac.resident > 0 && cus > 0 && (long)tac.grid * L <= (long)cus * tac.resident;
     p.owner_wait = all_resident ? owner_wait_ticks() : 0u;
+    p.health = wsp.cnt != nullptr ? wsp.cnt + wsp.cnt_count : nullptr;
     p.L = L;
     p.bw = batch.bw;
     p.bws = batch.bws;
@@ -364,6 +366,32 @@ SKGEMM_API int skgemm_set_timeline(void* buf, size_t capacity) {
   g_stamps_cap.store(buf ? capacity : 0);
   g_stamps.store(static_cast<uint64_t*>(buf));
   return SKGEMM_OK;
+}
+
+SKGEMM_API int skgemm_health(uint32_t* words, size_t n_words, hipStream_t stream) {
+  if (words == nullptr && n_words > 0) return SKGEMM_EINVAL;
+  for (size_t i = 0; i < n_words; ++i) words[i] = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  Workspace w;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    auto it = g_ws.find(std::make_pair(dev, stream));
+    if (it == g_ws.end() || it->second.cnt == nullptr) return SKGEMM_OK;  // nothing ran yet
+    w = it->second;
+  }
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &st);
+  if (e != hipSuccess) return hip_fail(e);
+  if (st != hipStreamCaptureStatusNone) return SKGEMM_EINVAL;
+  uint32_t* health = w.cnt + w.cnt_count;
+  const size_t n = std::min(n_words, (size_t)skg::kHealthWords);
+  e = hipStreamSynchronize(stream);
+  if (e == hipSuccess && n > 0) e = hipMemcpy(words, health, n * sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemsetAsync(health, 0, skg::kHealthWords * sizeof(uint32_t), stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return e == hipSuccess ? SKGEMM_OK : hip_fail(e);
 }
 
 SKGEMM_API int skgemm_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {

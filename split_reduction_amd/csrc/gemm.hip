@@ -805,6 +805,7 @@ void splitk_stream_kernel(GemmParams p) {
                                                      __HIP_MEMORY_SCOPE_AGENT);
           ready = (old & kArrivals) == (uint32_t)S;  // all arrived meanwhile: still ours
           pending = false;
+          if (p.owner_wait > 0) note_timeout(p.health, (uint32_t)tile, (uint32_t)rank, p.owner_wait);
         }
         break;
       }

@@ -19,6 +19,7 @@ struct GemmParams {
   int kc;       // K elements of X staged in LDS at a time; divides ks
   int nchunks;  // ks / kc
   uint64_t* stamps;  // optional per-workgroup phase stamps
+  uint32_t* health;     // owner time-outs: [0] count, [8 + 8r ..] record r (workspace)
   uint32_t owner_wait;  // device-clock ticks (100 MHz) a tile's owner waits for
                         // the other ranks before handing the tile to the last
                         // to arrive (0: hand over at once)
@@ -29,6 +30,28 @@ struct GemmParams {
   uint64_t bpart;            // floats between problems' partials
   uint32_t bcnt;             // counters between problems' counters
 };
+
+// Health words of a workspace: word 0 counts owner waits that ran out of time
+// (the tile then went to the last rank to arrive); words 8 + 8r .. 8 + 8r + 4
+// hold the first kHealthRecords of them: {1, first 16-row group of the tile,
+// owner rank, problem, ticks waited}.
+constexpr int kHealthRecords = 15;
+constexpr int kHealthWords = 8 + 8 * kHealthRecords;
+
+// Records one owner time-out (vector atomics and stores only).
+__device__ __forceinline__ void note_timeout(uint32_t* health, uint32_t group, uint32_t rank,
+                                             uint32_t waited) {
+  if (health == nullptr) return;
+  const uint32_t slot = __hip_atomic_fetch_add(health, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (slot < (uint32_t)kHealthRecords) {
+    uint32_t* r = health + 8 + 8 * slot;
+    r[1] = group;
+    r[2] = rank;
+    r[3] = blockIdx.y;
+    r[4] = waited;
+    __hip_atomic_store(r, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
 // Moves p's pointers to the problem of this workgroup (blockIdx.y).
 __device__ __forceinline__ void select_problem(GemmParams& p) {

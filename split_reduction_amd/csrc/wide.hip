@@ -268,7 +268,11 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
         }
         if (__builtin_amdgcn_s_memrealtime() > deadline) {
           uint32_t o2 = 0;
-          if (lane == 0) o2 = __hip_atomic_fetch_or(cnt, kAbandon, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (lane == 0) {
+            o2 = __hip_atomic_fetch_or(cnt, kAbandon, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (p.owner_wait > 0)
+              note_timeout(p.health, (uint32_t)(n0 / 16 + wn * RG), (uint32_t)rank, p.owner_wait);
+          }
           o2 = __builtin_amdgcn_readfirstlane(o2);
           finish = (o2 & kArrivals) == (uint32_t)S;  // all arrived meanwhile: still ours
           break;

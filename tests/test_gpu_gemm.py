@@ -394,7 +394,8 @@ def test_owner_handover(wait, shape, monkeypatch):
     """The persistent kernel's tile owners wait as usual, give up at once, or
     after one tick and hand their tiles to the last rank to arrive: results
     must be unchanged, several launches in a row (the counters end each
-    launch at 0)."""
+    launch at 0), and the health report holds well-formed records of the
+    waits that ran out (none for the normal wait)."""
     monkeypatch.setenv("SKGEMM_KIND", "1")
     monkeypatch.setenv("SKGEMM_STREAM", shape)
     monkeypatch.setenv("SKGEMM_OWNER_WAIT", wait)
@@ -405,8 +406,17 @@ def test_owner_handover(wait, shape, monkeypatch):
         x, w = workloads.small_bf16_case(T, K, N, seed=8000 + T + S)
         ref = G.gemm_bf16_ref(x, w)
         W = to_dev_bf16(w)
+        sk.skgemm_health()  # clear
         for rep in range(3):
             assert_parity(run_bf16(x, None, S, W=W), ref, K, f"hand-over T={T} S={S} rep {rep}")
+        h = sk.skgemm_health()
+        log(f"  health: {h['timeouts']} time-outs, first records {h['records'][:3]}")
+        # Every record names a real tile group and owner rank; a time-out is
+        # recorded only for a wait that was armed and ran out.
+        for (group, rank, problem, ticks) in h["records"]:
+            assert group < N // 16 and rank < S and problem == 0 and ticks == int(wait)
+        if wait in ("0", "10000"):
+            assert h["timeouts"] == 0
 
 
 WIDE_CASES = [(40, 512, 4096, 4), (100, 256, 2048, 2), (128, 768, 1024, 1), (64, 512, 8192, 8),
@@ -562,3 +572,31 @@ def test_timeline_stamps(monkeypatch):
     buf.zero_()
     run_bf16(x, wb, w.split_k)
     assert int(buf.abs().sum().item()) == 0
+
+
+def test_health_records_timeouts():
+    """With a one-tick owner wait on a shape with many tiles per owner, some
+    waits run out: the report counts them, names their tiles and clears."""
+    t = torch()
+    import os
+    os.environ["SKGEMM_OWNER_WAIT"] = "1"
+    os.environ["SKGEMM_KIND"] = "1"
+    os.environ["SKGEMM_STREAM"] = "0"
+    try:
+        T, N, K, S = 8, 8192, 4096, 8
+        x, w = workloads.small_bf16_case(T, K, N, seed=8100)
+        W, X = to_dev_bf16(w), to_dev_bf16(x)
+        C = empty_bf16(T, N)
+        sk.skgemm_health()
+        log(f"health: T={T} N={N} K={K} S={S} tactic={sk.skgemm_tactic_for(T, N, K, S)}")
+        for _ in range(5):
+            sk.skgemm_bf16(W, X, C, T, N, K, S)
+        t.cuda.synchronize()
+        h = sk.skgemm_health()
+        log(f"  {h['timeouts']} time-outs, records {h['records'][:4]}")
+        assert h["timeouts"] >= 1 and len(h["records"]) == min(h["timeouts"], 15)
+        assert_parity(bf16_bits(C), G.gemm_bf16_ref(x, w), K, "after time-outs")
+        assert sk.skgemm_health()["timeouts"] == 0  # cleared
+    finally:
+        for k in ("SKGEMM_OWNER_WAIT", "SKGEMM_KIND", "SKGEMM_STREAM"):
+            os.environ.pop(k, None)
