@@ -367,12 +367,12 @@ PMC_LAUNCHES = 10
 PMC_COPIES = 5
 
 
-def pmc_run() -> None:
+def pmc_run(name: str = HEADLINE) -> None:
     import torch
 
     import split_reduction_amd as sk
 
-    head = workloads.WORKLOADS[HEADLINE]
+    head = workloads.get(name)
     case = Case(head)
     stream = torch.cuda.current_stream()
     for i in range(PMC_LAUNCHES):
@@ -385,11 +385,11 @@ def pmc_run() -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     del sk
-    print(json.dumps({"pmc_run": HEADLINE, "launches": PMC_LAUNCHES, "copies": PMC_COPIES,
+    print(json.dumps({"pmc_run": name, "launches": PMC_LAUNCHES, "copies": PMC_COPIES,
                       "copy_bytes": COPY_BYTES}))
 
 
-def pmc_summary(path: str) -> dict:
+def pmc_summary(path: str, name: str = HEADLINE) -> dict:
     """HBM bytes per headline launch from the FETCH_SIZE and WRITE_SIZE passes
     of ``--pmc-run`` under ``path`` (KiB per dispatch, each scaled by what the
     same counter reads for the 256 MiB calibration copies: the last
@@ -417,10 +417,10 @@ def pmc_summary(path: str) -> dict:
     write_factor = write_copy * 1024 / COPY_BYTES
     rd = fetch * 1024 / fetch_factor
     wr = write * 1024 / write_factor
-    head = workloads.WORKLOADS[HEADLINE]
+    head = workloads.get(name)
     algo = head.weight_bytes() + head.T * head.K * 2 + head.T * head.N * 2
     out = {
-        "workload": HEADLINE,
+        "workload": name,
         "kernel": kname.split("(")[0].replace("void ", ""),
         "kernel_source_sha": kernel_source_hash(),
         "fetch_size_kib_per_launch": round(fetch, 1),
@@ -438,10 +438,10 @@ def pmc_summary(path: str) -> dict:
         "algorithmic_bytes_per_launch": algo,
         "commands": [
             "cd /tmp && timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE --output-format csv "
-            "-d $R/gpurun_out/pmc/fetch -o fetch -- python3 $R/bench.py --pmc-run",
+            f"-d $R/gpurun_out/pmc/fetch -o fetch -- python3 $R/bench.py --pmc-run {name}",
             "cd /tmp && timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE --output-format csv "
-            "-d $R/gpurun_out/pmc/write -o write -- python3 $R/bench.py --pmc-run",
-            "python bench.py --pmc-summary gpurun_out/pmc",
+            f"-d $R/gpurun_out/pmc/write -o write -- python3 $R/bench.py --pmc-run {name}",
+            f"python bench.py --pmc-summary gpurun_out/pmc {name}",
         ],
         "note": (f"R is the repository root. Counters are per dispatch: {PMC_LAUNCHES} headline "
                  f"launches on rotated weights, then {PMC_COPIES} copies of {COPY_BYTES >> 20} MiB "
@@ -475,14 +475,16 @@ def main() -> None:
     ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-summary", metavar="DIR", help="summarise a rocprofv3 kernel trace and exit")
-    ap.add_argument("--pmc-run", action="store_true", help="the short run HBM counters are taken on")
-    ap.add_argument("--pmc-summary", metavar="DIR", help="summarise rocprofv3 counter CSVs and exit")
+    ap.add_argument("--pmc-run", nargs="?", const=HEADLINE, metavar="WORKLOAD",
+                    help="the short run HBM counters are taken on (default: the headline)")
+    ap.add_argument("--pmc-summary", nargs="+", metavar=("DIR", "WORKLOAD"),
+                    help="summarise rocprofv3 counter CSVs under DIR (for WORKLOAD) and exit")
     args = ap.parse_args()
     if args.pmc_summary:
-        pmc_summary(args.pmc_summary)
+        pmc_summary(*args.pmc_summary[:2])
         return
     if args.pmc_run:
-        pmc_run()
+        pmc_run(args.pmc_run)
         return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.steps, args.warmup)
