@@ -65,6 +65,12 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
   constexpr int STEP_K = F * PIECE_K;          // K elements of one load step
   constexpr int SUB_K = MX ? 8 : 32 * F;       // K distance between a lane's sub-steps
   constexpr int D = cluster_depth(NT, C, MX);
+  // Weight loads in whole 128-byte lines: a fold of F >= 2 already covers
+  // 64*F contiguous bytes of each of its R rows per instruction; unfolded
+  // bf16 with two pieces loads rows 0-7 and 8-15 as a line pair instead and
+  // rearranges at use. Whole-line loads carry the non-temporal hint.
+  constexpr bool LINES = F == 1 && !MX && C == 2;
+  constexpr int WPOL = (F >= 2 || LINES) ? kPolicyStream : kPolicyDefault;
   static_assert(F == 1 || NT == 1, "folding needs a single token tile");
   static_assert(R >= 2, "outputs are stored in row pairs");
 
@@ -111,7 +117,7 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
   const rsrc_t cr = make_rsrc(p.c, (uint32_t)T * (uint32_t)N * 2u);
 
   // Byte offsets that do not change with the step.
-  const uint32_t a_row = (uint32_t)ra * wrow_bytes;
+  const uint32_t a_row = LINES ? line_pair_offset(li, 0, wrow_bytes) : (uint32_t)ra * wrow_bytes;
   const uint32_t s_row = (uint32_t)ra * (uint32_t)(K / 32);
   // K offset of a lane's first piece within a step. bf16: piece l of the
   // lane in fold f, K block g covers ((l*F + f)*4 + g)*8 .. +7, so one load
@@ -136,10 +142,11 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
     int ir = i + rot;
     if (ir >= n_i) ir -= n_i;
     const int kel = kbase + (sub + WR * ir) * STEP_K;
-    const uint32_t a_off = elem_byte(WF, (uint32_t)(kel + a_k));
+    // Line pairs: window li / 8 sits in a_row, so the lane's K block is g.
+    const uint32_t a_off = elem_byte(WF, (uint32_t)(kel + (LINES ? 8 * g : a_k)));
 #pragma unroll
     for (int l = 0; l < LOADS; ++l)
-      ra_ring[slot][l] = ld16_if(ok, wr, a_row + a_off + (uint32_t)(2 * SUB_K * l));
+      ra_ring[slot][l] = ld16_if<WPOL>(ok, wr, a_row + a_off + (LINES ? 8u * wrow_bytes : (uint32_t)(2 * SUB_K)) * l);
     if constexpr (MX) sc_ring[slot] = ld1_if(ok, sr, s_row + (uint32_t)((kel + a_k) / 32));
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
@@ -153,13 +160,20 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int slot) {
+    u32x4 a[LOADS];
+    if constexpr (LINES) {
+      line_pair_to_operands(ra_ring[slot][0], ra_ring[slot][1], a[0], a[1]);
+    } else {
+#pragma unroll
+      for (int l = 0; l < LOADS; ++l) a[l] = ra_ring[slot][l];
+    }
 #pragma unroll
     for (int s2 = 0; s2 < SUBS; ++s2) {
       bf16x8 af;
       if constexpr (MX) {
-        af = decode_operand<WF>(ra_ring[slot][0], s2, e8m0_f32(sc_ring[slot]));
+        af = decode_operand<WF>(a[0], s2, e8m0_f32(sc_ring[slot]));
       } else {
-        af = as_bf16x8(ra_ring[slot][s2]);
+        af = as_bf16x8(a[s2]);
       }
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma_bf16(af, as_bf16x8(rb_ring[slot][tt][s2]), acc[tt]);
@@ -277,7 +291,7 @@ hipError_t launch_cluster_f(const Tactic& t, const GemmParams& p, hipStream_t s)
 
 }  // namespace
 
-bool cluster_fits(int T, int N, int ks, int S, int wf, int max_fold, int force_c, Tactic* t) {
+bool cluster_fits(int T, int N, int ks, int S, int wf, int max_fold, int force_c, Tactic* t, int L) {
   const bool mx = wf != kBf16;
   if (T < 1 || T > 32 || S > kClusterMaxRanks || ks <= 0) return false;
   const int nt = (T + 15) / 16;
@@ -289,6 +303,10 @@ bool cluster_fits(int T, int N, int ks, int S, int wf, int max_fold, int force_c
     fold = 16 / tp;
     if (fold > 8) fold = 8;
   }
+  // Taller tiles while the grid still covers every CU: each workgroup reads
+  // all of X, so halving the fold halves the X re-reads (measured T=8,
+  // K=7168, N=4096: 16-row tiles 16.3 us, 8-row tiles 21.8 us).
+  while (fold > 1 && (long)(N / (32 / fold)) * L >= kChipCUs) fold /= 2;
   if (fold > max_fold) fold = max_fold;
   for (int c = 2; c >= 1; --c) {
     if (mx && c == 2) continue;  // one 16-byte MXFP4 piece is a whole step

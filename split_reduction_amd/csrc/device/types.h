@@ -70,6 +70,32 @@ __device__ __forceinline__ u32x4 ld16_coherent_if(bool ok, rsrc_t r, uint32_t of
   return __builtin_amdgcn_raw_buffer_load_b128(r, ok ? off : kOOB, 0, kPolicyDeviceCoherent);
 }
 
+// Whole-line weight loads. A v_mfma_f32_16x16x32 A operand holds, in lane
+// (li = lane % 16, g = lane / 16), 16 bytes of row li at K block g, so a load
+// straight into operand layout covers 16 rows x 64 bytes: half of each
+// 128-byte line, and streaming such halves reaches ~4.9 TB/s where whole
+// lines with the non-temporal hint reach ~6.4 TB/s (measured, 264 MB). The
+// pair below loads rows 0-7 (load 0) and rows 8-15 (load 1) instead, lane
+// (li, g) taking row li % 8 + 8 * load at 64-byte window li / 8, block g:
+// 8 whole lines per instruction. One DPP move per register (rotate by 8
+// lanes inside each 16-lane row, written to half the lanes) turns the pair
+// into the two 16-row operands, of windows 0 and 1.
+//
+// Byte offset of lane (li, g) within load 0, relative to row 0, window 0.
+__device__ __forceinline__ uint32_t line_pair_offset(int li, int g, uint32_t row_bytes) {
+  return (uint32_t)(li & 7) * row_bytes + 64u * (uint32_t)(li >> 3) + 16u * (uint32_t)g;
+}
+__device__ __forceinline__ void line_pair_to_operands(u32x4 l0, u32x4 l1, u32x4& w0, u32x4& w1) {
+  constexpr int kRowRor8 = 0x128;  // DPP row_ror:8
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // Lanes 8-15 of each row (banks 2, 3) take load 1's rows 8-15, window 0.
+    w0[e] = (uint32_t)__builtin_amdgcn_update_dpp((int)l0[e], (int)l1[e], kRowRor8, 0xF, 0xC, false);
+    // Lanes 0-7 (banks 0, 1) take load 0's rows 0-7, window 1.
+    w1[e] = (uint32_t)__builtin_amdgcn_update_dpp((int)l1[e], (int)l0[e], kRowRor8, 0xF, 0x3, false);
+  }
+}
+
 // Waits until every vector memory access this wave issued has completed
 // (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -376,6 +376,10 @@ void splitk_stream_kernel(GemmParams p) {
   constexpr int SWK = EPI ? WK - 1 : WK;   // streaming waves per tile
   constexpr int PARKED = EPI ? SWK : WK - 1;  // partial sums parked in LDS per tile
   constexpr int RED_QUADS = (PARKED > 0 ? PARKED : 1) * NT * 64;  // one parity half
+  // bf16 with two pieces per step: whole-line loads (rows 0-7, rows 8-15),
+  // turned into the two operands at use, with the non-temporal hint.
+  constexpr bool LINES = !MX && C == 2;
+  constexpr int WPOL = LINES ? kPolicyStream : kPolicyDefault;
   static_assert(WK == 1 || WN == 1, "waves that split a tile form one column");
   static_assert(!EPI || WK > 1, "an epilogue wave needs streaming waves");
 
@@ -422,7 +426,8 @@ void splitk_stream_kernel(GemmParams p) {
 
   // ---- weight ring (streaming waves) -------------------------------------
   int pf_i = 0;
-  uint32_t pf_row = (uint32_t)(col * 16 + li) * wrow_bytes;
+  uint32_t pf_row = LINES ? (uint32_t)(col * 16) * wrow_bytes + line_pair_offset(li, 0, wrow_bytes)
+                          : (uint32_t)(col * 16 + li) * wrow_bytes;
   uint32_t pf_srow = (uint32_t)(col * 16 + li) * (uint32_t)(K / 32);
   const uint32_t row_step = (uint32_t)(cstride * 16) * wrow_bytes;
   const uint32_t srow_step = (uint32_t)(cstride * 16) * (uint32_t)(K / 32);
@@ -434,7 +439,8 @@ void splitk_stream_kernel(GemmParams p) {
     const int kel = kbase + (sw + SWK * pf_i) * STEP_K;
     const uint32_t lo = elem_byte(WF, (uint32_t)kel) + 16u * g;
 #pragma unroll
-    for (int l = 0; l < LOADS; ++l) ring[slot][l] = ld16_if(ok, wr, pf_row + lo + 64 * l);
+    for (int l = 0; l < LOADS; ++l)
+      ring[slot][l] = ld16_if<WPOL>(ok, wr, pf_row + lo + (LINES ? 8u * wrow_bytes : 64u) * l);
     if constexpr (MX) sring[slot] = ld1_if(ok, sr, pf_srow + (uint32_t)((kel + LK * g) / 32));
     ++issued;
     if (++pf_i == n_i) {
@@ -445,9 +451,9 @@ void splitk_stream_kernel(GemmParams p) {
   };
 
   // ---- stage this rank's X slice once ------------------------------------
-  // The first batch of X loads goes out before the weight prologue, so its
-  // LDS writes wait only for X (loads complete in issue order) and the
-  // multiplies can start while the weights are still arriving.
+  // The weight prologue goes out only once the slice is in LDS: issued
+  // together, the two share the CU's intake and the slice, which every
+  // multiply waits for, lands late (measured 0.3-2 us slower per launch).
   // Workgroups of one rank that share an XCD stage the same slice at the same
   // time; each starts at a different point of it (a rotation of the piece
   // order) so that their requests for the same lines do not queue on one L2
@@ -489,10 +495,6 @@ void splitk_stream_kernel(GemmParams p) {
   {
     u32x4 v[XBATCH];
     stage_load(tid, v);
-    if (!epi_wave) {
-#pragma unroll
-      for (int s = 0; s < D; ++s) issue(s);
-    }
     stage_store(tid, v);
     for (int p0 = tid + THREADS * XBATCH; p0 < pieces; p0 += THREADS * XBATCH) {
       stage_load(p0, v);
@@ -500,6 +502,10 @@ void splitk_stream_kernel(GemmParams p) {
     }
   }
   __syncthreads();
+  if (!epi_wave) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) issue(s);
+  }
   stamp[1] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
 
   // Thread 0 of each workgroup writes the stamps (vector stores).
@@ -602,8 +608,15 @@ void splitk_stream_kernel(GemmParams p) {
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const u32x4 (&a)[LOADS], uint32_t sc, int i) {
+  auto compute = [&](const u32x4 (&ld)[LOADS], uint32_t sc, int i) {
     const int j = sw + SWK * i;
+    u32x4 a[LOADS];
+    if constexpr (LINES) {
+      line_pair_to_operands(ld[0], ld[1], a[0], a[1]);
+    } else {
+#pragma unroll
+      for (int l = 0; l < LOADS; ++l) a[l] = ld[l];
+    }
 #pragma unroll
     for (int s2 = 0; s2 < SUBS; ++s2) {
       bf16x8 b[NT];
@@ -1018,7 +1031,7 @@ bool stream_fits(int si, int T, int N, int ks, int S, int wf, Tactic* t, int L =
   if (per_cu > stream_wgs_per_cu(t->nt)) per_cu = stream_wgs_per_cu(t->nt);
   per_cu = env_int("SKGEMM_WG_PER_CU", per_cu);
   if (per_cu < 1) per_cu = 1;
-  long g = (256L * per_cu) / ((long)S * (L > 0 ? L : 1));  // the whole batch resident
+  long g = ((long)kChipCUs * per_cu) / ((long)S * (L > 0 ? L : 1));  // the whole batch resident
   const long g_max = (n_tiles + c.wn - 1) / c.wn;  // every column gets a tile
   if (g > g_max) g = g_max;
   if (g < 1) g = 1;
@@ -1054,7 +1067,7 @@ bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L) {
   const int kind = env_int("SKGEMM_KIND", -1);
   if (kind == 2 || kind < 0) {
     Tactic c = t;
-    if (cluster_fits(tr, N, ks, S, wf, env_int("SKGEMM_FOLD", 8), env_int("SKGEMM_CLUSTER_C", 0), &c)) {
+    if (cluster_fits(tr, N, ks, S, wf, env_int("SKGEMM_FOLD", 8), env_int("SKGEMM_CLUSTER_C", 0), &c, L)) {
       // Whole tiles per workgroup pay off while the grid is about one
       // workgroup per CU; beyond, the persistent kernel's staged activations
       // and amortised ramp-up win. Every cluster workgroup re-reads all of X

@@ -97,10 +97,13 @@ struct Tactic {
 // fits (never for validated shapes).
 bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L = 1);
 
+// Compute units of an MI355X: the grid a launch needs to occupy the chip.
+constexpr int kChipCUs = 256;
+
 // Fills the configuration of the one-workgroup-per-tile kernel (kind 2) for a
-// launch over T <= 32 rows, folding at most max_fold ways (force_c > 0 pins
-// the pieces per lane for bf16); false if it does not apply.
-bool cluster_fits(int T, int N, int ks, int S, int wf, int max_fold, int force_c, Tactic* t);
+// launch over T <= 32 rows of L problems, folding at most max_fold ways
+// (force_c > 0 pins the pieces per lane for bf16); false if it does not apply.
+bool cluster_fits(int T, int N, int ks, int S, int wf, int max_fold, int force_c, Tactic* t, int L = 1);
 hipError_t launch_cluster(const Tactic& t, const GemmParams& p, hipStream_t stream);
 
 // Fills the configuration of the wide-tile kernel (kind 3) for 33 <= T <= 128
