@@ -16,8 +16,10 @@
 //    of chunk c + 1 go out at the start of chunk c, into registers, and are
 //    written to the other buffer when chunk c is done; one barrier per chunk.
 //  * Each wave streams its 32 weight rows over the whole K slice through a
-//    D-step register ring that runs on across chunk boundaries (weights do not
-//    depend on the chunk), 16-byte buffer loads straight into MFMA A operands.
+//    register ring that runs on across chunk boundaries (weights do not
+//    depend on the chunk). A slot holds two load steps as whole-line loads
+//    (rows 0-7 and 8-15 of each 16-row group over both steps' 64-byte
+//    windows), rearranged into MFMA A operands at use.
 //  * Hand-off per wave column (32 rows x T): the column's partial goes to
 //    the workspace with device-coherent stores, the wave bumps the column's
 //    arrival counter, and one owner rank per column, (column + tile) mod S,
@@ -52,10 +54,16 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
   constexpr int STEP_K = MX ? 4 * LK : 32;    // K elements of one load step
   constexpr int KC = wide_kc(NT);
   constexpr int CS = KC / STEP_K;             // load steps per chunk
-  // Ring depth in load steps (divides CS): 8 steps = 16 KiB of weights in
-  // flight per wave, 4 where the accumulators of many tokens need the registers.
-  constexpr int D = MX ? (CS < 4 ? CS : 4) : 8;
-  static_assert(CS % D == 0, "ring slots repeat every chunk");
+  // A ring slot holds two load steps: per 16-row group, rows 0-7 and rows
+  // 8-15 over both steps' 64-byte windows, one whole 128-byte line per row
+  // and instruction (non-temporal), rearranged into the two steps' operands
+  // at use.
+  constexpr int CS2 = CS / 2;                 // ring slots per chunk
+  static_assert(CS % 2 == 0, "a chunk holds whole step pairs");
+  // Ring depth in slots (divides CS2): 4 slots = 16 KiB of weights in flight
+  // per wave (bf16), fewer where the decode and its registers are heavier.
+  constexpr int D = MX ? (CS2 < 2 ? CS2 : 2) : 4;
+  static_assert(CS2 % D == 0, "ring slots repeat every chunk");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -76,7 +84,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
   const int n0 = tile * kWideRows;
   const int kbase = rank * p.ks;
   const int nchunks = p.ks / KC;
-  const int total = nchunks * CS;  // load steps of this wave
+  const int total = nchunks * CS2;  // ring slots (step pairs) of this wave
 
   const uint32_t wrow_bytes = row_bytes(WF, (uint32_t)K);
   const rsrc_t wr = make_rsrc(static_cast<const uint8_t*>(p.w) + (size_t)n0 * wrow_bytes,
@@ -88,22 +96,27 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
   uint32_t row_off[RG], srow_off[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
-    const uint32_t row = (uint32_t)((wn * RG + rg) * 16 + li);
-    row_off[rg] = row * wrow_bytes;
-    srow_off[rg] = row * (uint32_t)(K / 32);
+    const uint32_t row0 = (uint32_t)((wn * RG + rg) * 16);
+    row_off[rg] = row0 * wrow_bytes + line_pair_offset(li, 0, wrow_bytes);
+    srow_off[rg] = (row0 + (uint32_t)li) * (uint32_t)(K / 32);  // scales: operand layout
   }
 
   // ---- weight ring ----------------------------------------------------------
-  u32x4 ring[D][RG];
-  uint32_t sring[D][RG];
+  u32x4 ring[D][RG][2];
+  uint32_t sring[D][RG][2];
   auto issue = [&](int slot, int q) {
     const bool ok = q < total;
-    const int kel = kbase + q * STEP_K;
+    const int kel = kbase + q * 2 * STEP_K;
     const uint32_t lo = elem_byte(WF, (uint32_t)kel) + 16u * g;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      ring[slot][rg] = ld16_if(ok, wr, row_off[rg] + lo);
-      if constexpr (MX) sring[slot][rg] = ld1_if(ok, sr, srow_off[rg] + (uint32_t)((kel + LK * g) / 32));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ring[slot][rg][h] = ld16_if<kPolicyStream>(ok, wr, row_off[rg] + lo + 8u * wrow_bytes * h);
+      if constexpr (MX) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w)
+          sring[slot][rg][w] = ld1_if(ok, sr, srow_off[rg] + (uint32_t)((kel + w * STEP_K + LK * g) / 32));
+      }
     }
   };
 
@@ -154,24 +167,32 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt) acc[rg][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int slot, int c, int j) {
+  // Slot jp of chunk c: load steps 2*jp and 2*jp + 1 of the chunk.
+  auto compute = [&](int slot, int c, int jp) {
     const uint8_t* buf = smem + (c & 1) * CHUNK_BYTES;
+    u32x4 a[RG][2];
 #pragma unroll
-    for (int s2 = 0; s2 < SUBS; ++s2) {
-      bf16x8 b[NT];
+    for (int rg = 0; rg < RG; ++rg) line_pair_to_operands(ring[slot][rg][0], ring[slot][rg][1], a[rg][0], a[rg][1]);
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
-        b[tt] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + x_slot(j, s2, g, tt * 16 + li) * 16));
+    for (int w = 0; w < 2; ++w) {
+      const int j = 2 * jp + w;
 #pragma unroll
-      for (int rg = 0; rg < RG; ++rg) {
-        bf16x8 af;
-        if constexpr (MX) {
-          af = decode_operand<WF>(ring[slot][rg], s2, e8m0_f32(sring[slot][rg]));
-        } else {
-          af = as_bf16x8(ring[slot][rg]);
+      for (int s2 = 0; s2 < SUBS; ++s2) {
+        bf16x8 b[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          b[tt] = as_bf16x8(*reinterpret_cast<const u32x4*>(buf + x_slot(j, s2, g, tt * 16 + li) * 16));
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          bf16x8 af;
+          if constexpr (MX) {
+            af = decode_operand<WF>(a[rg][w], s2, e8m0_f32(sring[slot][rg][w]));
+          } else {
+            af = as_bf16x8(a[rg][w]);
+          }
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) acc[rg][tt] = mfma_bf16(af, b[tt], acc[rg][tt]);
         }
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) acc[rg][tt] = mfma_bf16(af, b[tt], acc[rg][tt]);
       }
     }
   };
@@ -189,10 +210,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
     const bool next = c + 1 < nchunks;
     if (next) x_load(c + 1);
 #pragma unroll
-    for (int j = 0; j < CS; ++j) {
-      const int slot = j % D;
-      compute(slot, c, j);
-      issue(slot, c * CS + j + D);
+    for (int jp = 0; jp < CS2; ++jp) {
+      const int slot = jp % D;
+      compute(slot, c, jp);
+      issue(slot, c * CS2 + jp + D);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (next) {
