@@ -124,15 +124,34 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
   // instruction covers 64*F contiguous bytes of each row. Block-scaled: the
   // lane's LK codes cover (f*4 + g)*LK .. +LK-1.
   const int a_k = (fa * 4 + g) * (MX ? LK : 8);
-  const int b_k = (fb * 4 + g) * (MX ? LK : 8);
+  // Activations (bf16). In operand layout neighbouring lanes hold different
+  // tokens, so no 4-lane group of a load reads contiguous bytes, and L2 hits
+  // move at half the rate of contiguous reads (measured). The loads therefore
+  // take contiguous runs (lane m: token m / 4F, 16-byte chunk m % 4F of the
+  // token's 64F bytes of the piece) and one ds_bpermute per register moves
+  // each lane's chunk to its operand lane (li, g): token li % TF, chunk
+  // (li / TF) * 4 + g. Used by folds 1 and 2 (T >= 5 tokens: re-reads as
+  // large as the weights); the short launches of folds 4 and 8 gain nothing
+  // and lose ~0.3 us to the extra code (measured T=1, K=1024).
+  constexpr bool xperm = !MX && F <= 2;
+  const int xt = xperm ? lane / (4 * F) : tb;                       // token of this lane's load
+  const int b_k = xperm ? (lane % (4 * F)) * 8 : (fb * 4 + g) * (MX ? LK : 8);
+  const int b_src = 4 * ((li % TF) * 4 * F + (li / TF) * 4 + g);    // bpermute byte address
   bool b_ok[NT];
   uint32_t b_row[NT];
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) {
-    const int t = tt * 16 + tb;
+    const int t = tt * 16 + xt;
     b_ok[tt] = t < T;
     b_row[tt] = (uint32_t)(b_ok[tt] ? t : 0) * (uint32_t)K * 2u;
   }
+  auto x_operand = [&](u32x4 v) -> bf16x8 {
+    if constexpr (xperm) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(b_src, (int)v[e]);
+    }
+    return as_bf16x8(v);
+  };
 
   u32x4 ra_ring[D][LOADS];
   uint32_t sc_ring[D];
@@ -176,7 +195,7 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
         af = as_bf16x8(a[s2]);
       }
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma_bf16(af, as_bf16x8(rb_ring[slot][tt][s2]), acc[tt]);
+      for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma_bf16(af, x_operand(rb_ring[slot][tt][s2]), acc[tt]);
     }
   };
 
