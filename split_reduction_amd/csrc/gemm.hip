@@ -157,24 +157,26 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
     if (c > 0) __syncthreads();  // every wave is done reading the previous chunk
 
     // Stage X[0:T, kc0 : kc0 + kc) in LDS. Consecutive threads take
-    // consecutive tokens of one 8-element piece, so writes are contiguous.
+    // consecutive 8-element pieces of one token, so every 4-lane group of a
+    // load reads one contiguous run.
     {
-      const int pieces = T * (p.kc / 8);
+      const int kp = p.kc / 8;  // pieces per token
+      const int pieces = T * kp;
       for (int p0 = tid; p0 < pieces; p0 += THREADS * XBATCH) {
         u32x4 v[XBATCH];
 #pragma unroll
         for (int b = 0; b < XBATCH; ++b) {
           const int pc = p0 + b * THREADS;
-          const int t = pc % T;
-          const int k = (pc / T) * 8;
+          const int t = pc / kp;
+          const int k = (pc - t * kp) * 8;
           v[b] = ld16_if(pc < pieces, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(kc0 + k)) * 2u);
         }
 #pragma unroll
         for (int b = 0; b < XBATCH; ++b) {
           const int pc = p0 + b * THREADS;
           if (pc < pieces) {
-            const int t = pc % T;
-            const int k = (pc / T) * 8;
+            const int t = pc / kp;
+            const int k = (pc - t * kp) * 8;
             int j, s, gg;
             if constexpr (MX) {
               j = k / STEP_K; gg = (k % STEP_K) / LK; s = (k % LK) / 8;
@@ -458,7 +460,10 @@ void splitk_stream_kernel(GemmParams p) {
   // time; each starts at a different point of it (a rotation of the piece
   // order) so that their requests for the same lines do not queue on one L2
   // channel together.
-  const int pieces = T * (p.ks / 8);
+  // Pieces are 16-byte chunks, K fastest (piece q: token q / kp, chunk
+  // q % kp), so every 4-lane group of a load reads one contiguous run.
+  const int kp = p.ks / 8;  // chunks per token
+  const int pieces = T * kp;
   const int rot = (int)(((unsigned)gi % 32u) * (unsigned)(pieces / 32));
   auto piece = [&](int pc) -> int {
     const int q = pc + rot;
@@ -469,8 +474,8 @@ void splitk_stream_kernel(GemmParams p) {
     for (int b = 0; b < XBATCH; ++b) {
       const int pc = p0 + b * THREADS;
       const int q = piece(pc);
-      const int t = q % T;
-      const int k = (q / T) * 8;
+      const int t = q / kp;
+      const int k = (q - t * kp) * 8;
       v[b] = ld16_if(pc < pieces, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(kbase + k)) * 2u);
     }
   };
@@ -480,8 +485,8 @@ void splitk_stream_kernel(GemmParams p) {
       const int pc = p0 + b * THREADS;
       if (pc < pieces) {
         const int q = piece(pc);
-        const int t = q % T;
-        const int k = (q / T) * 8;
+        const int t = q / kp;
+        const int k = (q - t * kp) * 8;
         int j, s2, gg;
         if constexpr (MX) {
           j = k / STEP_K; gg = (k % STEP_K) / LK; s2 = (k % LK) / 8;

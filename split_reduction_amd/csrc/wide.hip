@@ -121,7 +121,10 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
   };
 
   // ---- X chunks -------------------------------------------------------------
-  // Operand-ordered layout of one chunk over TP = 16 * NT token slots: slot
+  // Loads take 16-byte pieces K fastest (piece pc: token pc / (KC / 8),
+  // K offset 8 * (pc % (KC / 8))), so every 4-lane group reads one
+  // contiguous run. Operand-ordered layout of one chunk over TP = 16 * NT
+  // token slots: slot
   // ((j*SUBS + s)*4 + gg)*TP + t holds token t's 8 elements of load step j,
   // sub-step s, lane K block gg. Slots of tokens t >= T hold zeros (their
   // loads are out of range and read zero without a memory access), and every
@@ -137,8 +140,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
 #pragma unroll
     for (int b = 0; b < XP; ++b) {
       const int pc = tid + b * THREADS;
-      const int t = pc % TP;
-      const int k = (pc / TP) * 8;
+      const int t = pc / (KC / 8);
+      const int k = (pc % (KC / 8)) * 8;
       xreg[b] = ld16_if(pc < PIECES && t < T, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(k0 + k)) * 2u);
     }
   };
@@ -148,8 +151,8 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
     for (int b = 0; b < XP; ++b) {
       const int pc = tid + b * THREADS;
       if (PIECES % THREADS == 0 || pc < PIECES) {
-        const int t = pc % TP;
-        const int k = (pc / TP) * 8;
+        const int t = pc / (KC / 8);
+        const int k = (pc % (KC / 8)) * 8;
         int j, s2, gg;
         if constexpr (MX) {
           j = k / STEP_K; gg = (k % STEP_K) / LK; s2 = (k % LK) / 8;
