@@ -133,10 +133,24 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
   // (li / TF) * 4 + g. Used by folds 1 and 2 (T >= 5 tokens: re-reads as
   // large as the weights); the short launches of folds 4 and 8 gain nothing
   // and lose ~0.3 us to the extra code (measured T=1, K=1024).
+  //
+  // Block-scaled weights (folds 1 and 2): operand s2 of a lane's 16-byte
+  // piece covers elements g*LK + 8*s2 of the step window, so the activation
+  // operand s2 of the four lane rows would be four runs LK elements apart.
+  // The weight pieces are therefore transposed across the lane rows at use
+  // (transpose_pieces: operand s2 of lane row g becomes elements 32*s2 + 8*g),
+  // and activation load s2 takes, for each (token, fold) slot li', the 64
+  // contiguous bytes 32*s2 .. 32*s2 + 31 of its window (lane 4*li' + q takes
+  // the q-th 16 bytes); operand lane (li, g) reads load lane 4*li + g.
   constexpr bool xperm = !MX && F <= 2;
-  const int xt = xperm ? lane / (4 * F) : tb;                       // token of this lane's load
-  const int b_k = xperm ? (lane % (4 * F)) * 8 : (fb * 4 + g) * (MX ? LK : 8);
-  const int b_src = 4 * ((li % TF) * 4 * F + (li / TF) * 4 + g);    // bpermute byte address
+  constexpr bool MXT = MX && F <= 2;
+  constexpr int XSUB_K = MXT ? 32 : SUB_K;  // K distance between a lane's activation loads
+  const int xs = lane >> 2;                 // MXT: (token, fold) slot of this lane's load
+  const int xt = xperm ? lane / (4 * F) : (MXT ? xs % TF : tb);   // token of this lane's load
+  const int b_k = xperm ? (lane % (4 * F)) * 8
+                        : (MXT ? (xs / TF) * 4 * LK + 8 * (lane & 3) : (fb * 4 + g) * (MX ? LK : 8));
+  const int b_src = xperm ? 4 * ((li % TF) * 4 * F + (li / TF) * 4 + g)  // bpermute byte address
+                          : 4 * (4 * li + g);
   bool b_ok[NT];
   uint32_t b_row[NT];
 #pragma unroll
@@ -146,7 +160,7 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
     b_row[tt] = (uint32_t)(b_ok[tt] ? t : 0) * (uint32_t)K * 2u;
   }
   auto x_operand = [&](u32x4 v) -> bf16x8 {
-    if constexpr (xperm) {
+    if constexpr (xperm || MXT) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[e] = (uint32_t)__builtin_amdgcn_ds_bpermute(b_src, (int)v[e]);
     }
@@ -166,13 +180,20 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
 #pragma unroll
     for (int l = 0; l < LOADS; ++l)
       ra_ring[slot][l] = ld16_if<WPOL>(ok, wr, a_row + a_off + (LINES ? 8u * wrow_bytes : (uint32_t)(2 * SUB_K)) * l);
-    if constexpr (MX) sc_ring[slot] = ld1_if(ok, sr, s_row + (uint32_t)((kel + a_k) / 32));
+    if constexpr (MXT) {
+      // The scales of the lane's window (4*LK / 32 bytes): after the
+      // transpose, operand s2 lies in the window's block s2.
+      const uint32_t so = s_row + (uint32_t)((kel + fa * 4 * LK) / 32);
+      sc_ring[slot] = WF == kMxfp4 ? ld4_if(ok, sr, so) : ld2_if(ok, sr, so);
+    } else if constexpr (MX) {
+      sc_ring[slot] = ld1_if(ok, sr, s_row + (uint32_t)((kel + a_k) / 32));
+    }
 #pragma unroll
     for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
       for (int s2 = 0; s2 < SUBS; ++s2)
         rb_ring[slot][tt][s2] =
-            ld16_if(ok && b_ok[tt], xr, b_row[tt] + (uint32_t)(kel + b_k + SUB_K * s2) * 2u);
+            ld16_if(ok && b_ok[tt], xr, b_row[tt] + (uint32_t)(kel + b_k + XSUB_K * s2) * 2u);
   };
 
   f32x4 acc[NT];
@@ -182,6 +203,8 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
     u32x4 a[LOADS];
     if constexpr (LINES) {
       line_pair_to_operands(ra_ring[slot][0], ra_ring[slot][1], a[0], a[1]);
+    } else if constexpr (MXT) {
+      a[0] = transpose_pieces<WF>(ra_ring[slot][0]);
     } else {
 #pragma unroll
       for (int l = 0; l < LOADS; ++l) a[l] = ra_ring[slot][l];
@@ -190,7 +213,7 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
     for (int s2 = 0; s2 < SUBS; ++s2) {
       bf16x8 af;
       if constexpr (MX) {
-        af = decode_operand<WF>(a[0], s2, e8m0_f32(sc_ring[slot]));
+        af = decode_operand<WF>(a[0], s2, e8m0_f32(MXT ? (sc_ring[slot] >> (8 * s2)) & 0xFFu : sc_ring[slot]));
       } else {
         af = as_bf16x8(a[s2]);
       }

@@ -51,6 +51,15 @@ __device__ __forceinline__ uint32_t ld1_if(bool ok, rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, ok ? off : kOOB, 0, POLICY);
 }
 
+template <int POLICY = kPolicyDefault>
+__device__ __forceinline__ uint32_t ld4_if(bool ok, rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, ok ? off : kOOB, 0, POLICY);
+}
+template <int POLICY = kPolicyDefault>
+__device__ __forceinline__ uint32_t ld2_if(bool ok, rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, ok ? off : kOOB, 0, POLICY);
+}
+
 // Stores dropped (no branch) when !ok.
 __device__ __forceinline__ void st16_if(bool ok, u32x4 v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, ok ? off : kOOB, 0, kPolicyDefault);

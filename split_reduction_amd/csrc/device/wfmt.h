@@ -64,4 +64,44 @@ __device__ __forceinline__ bf16x8 decode_operand(u32x4 v, int s2, float scale) {
   }
 }
 
+// Piece transpose of a block-scaled weight step across the four lane rows
+// (g = lane / 16) of one A row. Natural pieces: lane row g holds the 16
+// bytes of elements [g*LK, g*LK + LK) of the step's 4*LK-element window, and
+// operand s2 of it is elements g*LK + 8*s2 .. +7. After the transpose,
+// operand s2 of lane row g is elements 32*s2 + 8*g .. +7, so that the
+// activation operand s2 of all four lane rows is one contiguous 64-byte run
+// per token (see the cluster kernel). Each swap exchanges one bit of the
+// lane row with one bit of the register index:
+//   v_permlane16_swap(a, b): odd rows of a <-> even rows of b (row bit 0),
+//   v_permlane32_swap(a, b): rows 2, 3 of a <-> rows 0, 1 of b (row bit 1).
+// MXFP4 (eight elements per dword): a 4 x 4 transpose of (lane row, dword).
+// MXFP8 (four per dword, operands are dword pairs): a rotation of the three
+// bits (lane row, pair) taking group 2*g + p to position (row g, pair p).
+template <int WF>
+__device__ __forceinline__ u32x4 transpose_pieces(u32x4 v) {
+  auto swap16 = [](uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+  };
+  auto swap32 = [](uint32_t& a, uint32_t& b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+  };
+  uint32_t d0 = v[0], d1 = v[1], d2 = v[2], d3 = v[3];
+  if constexpr (WF == kMxfp4) {
+    swap32(d0, d2);  // row bit 1 <-> dword bit 1
+    swap32(d1, d3);
+    swap16(d0, d1);  // row bit 0 <-> dword bit 0
+    swap16(d2, d3);
+  } else {
+    swap16(d0, d2);  // row bit 0 <-> pair bit
+    swap16(d1, d3);
+    swap32(d0, d2);  // row bit 1 <-> pair bit
+    swap32(d1, d3);
+  }
+  return u32x4{d0, d1, d2, d3};
+}
+
 }  // namespace skg
