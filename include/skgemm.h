@@ -225,9 +225,10 @@ SKGEMM_API int skgemm_health(uint32_t* words, size_t n_words, hipStream_t stream
 
 /*
  * skgemm_read_probe: a reference for the weight stream, not part of the
- * method: reads `bytes` of device memory at src once, with plain coalesced
- * 16-byte loads, 512 workgroups of 1024 lanes each reading one contiguous
- * block, and computes nothing from them. The time it takes is the
+ * method: reads `bytes` of device memory at src once, with coalesced 16-byte
+ * non-temporal loads, 1024 workgroups of 512 lanes each reading one
+ * contiguous block (the fastest streaming read measured on the chip), and
+ * computes nothing from them. The time it takes is the
  * streaming-read rate the GEMM kernels are compared with at the same byte
  * count. src: 16-byte aligned, bytes a multiple of 16. sink: device memory for
  * 512 uint32 words, which the probe does not normally write. Returns

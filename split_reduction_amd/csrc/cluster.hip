@@ -350,7 +350,20 @@ bool cluster_fits(int T, int N, int ks, int S, int wf, int max_fold, int force_c
   // K=7168, N=4096: 16-row tiles 16.3 us, 8-row tiles 21.8 us).
   while (fold > 1 && (long)(N / (32 / fold)) * L >= kChipCUs) fold /= 2;
   if (fold > max_fold) fold = max_fold;
-  for (int c = 2; c >= 1; --c) {
+  // Pieces per lane (bf16): two unless the tile is folded and one piece per
+  // lane still gives every wave at least four load steps (measured K=7168,
+  // S=4, T=5..8: 7.5-9.6 us with one piece against 8.4-10.7 us with two;
+  // K=2048, S=2: 5.9 against 5.5 us). Unfolded tiles keep two, which their
+  // whole-line load pairs need.
+  int c_first = 2;
+  if (!mx && fold >= 2 && ks % (fold * 32) == 0) {
+    const int cs1 = ks / (fold * 32);
+    int wt1 = 4;
+    while (wt1 < (S * cs1 < 16 ? S * cs1 : 16)) wt1 *= 2;
+    if (wt1 >= S && cs1 / (wt1 / S) >= 4) c_first = 1;
+  }
+  for (int ci = 0; ci < 2; ++ci) {
+    const int c = ci == 0 ? c_first : 3 - c_first;
     if (mx && c == 2) continue;  // one 16-byte MXFP4 piece is a whole step
     if (force_c > 0 && !mx && c != force_c) continue;
     for (int f = fold; f >= 1; f /= 2) {

@@ -1034,6 +1034,10 @@ bool stream_fits(int si, int T, int N, int ks, int S, int wf, Tactic* t, int L =
   const int waves = c.wk * c.wn;
   int per_cu = (int)((160L * 1024) / (lds > 0 ? lds : 1));
   if (per_cu > stream_wgs_per_cu(t->nt)) per_cu = stream_wgs_per_cu(t->nt);
+  // A single problem runs best with one workgroup per CU (measured: as fast
+  // or faster on every decode and sweep shape, up to 40 % at T=24..32,
+  // N=2048); batches keep the residency the LDS allows.
+  if (L == 1) per_cu = 1;
   per_cu = env_int("SKGEMM_WG_PER_CU", per_cu);
   if (per_cu < 1) per_cu = 1;
   long g = ((long)kChipCUs * per_cu) / ((long)S * (L > 0 ? L : 1));  // the whole batch resident
@@ -1080,8 +1084,13 @@ bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L) {
       // batch the cluster kernel stays only while that is small (measured:
       // T=1 K=1024 N=1024 batches run 1.1 vs 1.6 us a problem on it, the
       // T=8 K=7168 N=2048 ones 9.6 vs 6.4 us on the persistent kernel).
+      // An unfolded tile with fewer workgroups than CUs leaves the chip
+      // partly idle; the persistent kernel then wins (measured T=12..32,
+      // N=1024..2048: 9.6-15.6 us against 12.1-18.3 us). Folded tiles stay
+      // ahead even there (T=5..8, N=1024).
       const double x_per_w = (double)tr * 2.0 / ((double)c.tile_n * weight_bytes_per_elem(wf));
-      const bool small = L == 1 ? c.grid <= kClusterMaxGrid
+      const bool fills = c.fold >= 2 || c.grid >= kChipCUs;
+      const bool small = L == 1 ? (c.grid <= kClusterMaxGrid && fills)
                                 : (x_per_w <= 0.5 && (long)c.grid * L <= kClusterMaxBatchGrid);
       if (kind == 2 || small) {
         *out = c;

@@ -123,9 +123,11 @@ hipError_t launch_mxfp4_dequant(const void* wq, const void* ws, void* out, int N
                                 hipStream_t s);
 hipError_t launch_mxfp8_dequant(const void* wq, const void* ws, void* out, int N, int K,
                                 hipStream_t s);
-// Plain coalesced read of `bytes` (a multiple of 16) with kReadProbeBlocks
-// workgroups of 1024 lanes (two per CU); sink needs kReadProbeBlocks words.
-constexpr int kReadProbeBlocks = 512;
+// Coalesced non-temporal read of `bytes` (a multiple of 16) with
+// kReadProbeBlocks workgroups of 512 lanes (four per CU); sink needs
+// kReadProbeSinkWords words (workgroup b may write word b % that count).
+constexpr int kReadProbeBlocks = 1024;
+constexpr int kReadProbeSinkWords = 512;
 constexpr uint32_t kReadProbeMagic = 0x9E3779B9u;
 hipError_t launch_read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 
