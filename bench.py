@@ -241,12 +241,12 @@ def run_workload(wl, steps, warmup, host_w=None) -> dict:
     import split_reduction_amd as sk
 
     case = Case(wl, host_w)
-    batched = None
-    if wl.weight_bytes() <= BATCH_MAX_WEIGHT_BYTES:
-        batched = case.time_batched(BATCH_L, steps, warmup)
     cold = case.time(steps, warmup, rotate=True)
     hot = case.time(steps, warmup, rotate=False)
     probe = case.time(steps, warmup, rotate=True, probe=True)
+    batched = None
+    if wl.weight_bytes() <= BATCH_MAX_WEIGHT_BYTES:
+        batched = case.time_batched(BATCH_L, steps, warmup)
     probe_bytes = case.weights[0][0].numel() * case.weights[0][0].element_size()
     probe_tbps = probe_bytes / (probe["t_us"] * 1e-6) / 1e12
     tac = sk.skgemm_tactic_for(wl.T, wl.N, wl.K, wl.split_k, {"bf16": 0, "mxfp4": 1, "mxfp8": 2}[wl.kind])
@@ -323,9 +323,10 @@ def trace_summary(path: str, steps: int, warmup: int) -> None:
     """Per-kernel durations from a rocprofv3 kernel trace of this script.
 
     Dispatches are taken in time order and cut into runs of the same kernel
-    and grid. The first run is the headline workload: per timing pass, W eager
-    warmup launches, the graph's untimed first replay and its timed replay of
-    K launches; one cold (rotated weights) pass, then one cache-resident pass.
+    and grid. The first run is the headline workload's single launches: per
+    timing pass, W eager warmup launches, the graph's untimed first replay and
+    its timed replay of K launches; one cold (rotated weights) pass, then one
+    cache-resident pass. Its batched launches follow as a run of their own.
     """
     import csv
 
@@ -351,9 +352,12 @@ def trace_summary(path: str, steps: int, warmup: int) -> None:
         d = np.array(durs)
         short = name.replace("void skg::", "").replace("(skg::GemmParams)", "")
         print(f"{i:3d} {len(d):6d} {d.mean():9.3f} {np.median(d):9.3f} {d.min():9.3f} {grid:>8}  {short}")
-    if segs:
-        d = np.array(segs[0][1])
-        per_pass = warmup + 2 * steps
+    # The headline's single launches: the first run holding both timing
+    # passes (its batched launches, timed afterwards, form a run of their own).
+    per_pass = warmup + 2 * steps
+    head = [s for s in segs if len(s[1]) >= 2 * per_pass]
+    if head:
+        d = np.array(head[0][1])
         if len(d) >= 2 * per_pass:
             cold = d[warmup + steps:per_pass]
             hot = d[per_pass + warmup + steps:2 * per_pass]
