@@ -52,6 +52,10 @@ __device__ __forceinline__ uint32_t ld1_if(bool ok, rsrc_t r, uint32_t off) {
 }
 
 template <int POLICY = kPolicyDefault>
+__device__ __forceinline__ u32x2 ld8_if(bool ok, rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, ok ? off : kOOB, 0, POLICY);
+}
+template <int POLICY = kPolicyDefault>
 __device__ __forceinline__ uint32_t ld4_if(bool ok, rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, ok ? off : kOOB, 0, POLICY);
 }

@@ -378,10 +378,18 @@ void splitk_stream_kernel(GemmParams p) {
   constexpr int SWK = EPI ? WK - 1 : WK;   // streaming waves per tile
   constexpr int PARKED = EPI ? SWK : WK - 1;  // partial sums parked in LDS per tile
   constexpr int RED_QUADS = (PARKED > 0 ? PARKED : 1) * NT * 64;  // one parity half
-  // bf16 with two pieces per step: whole-line loads (rows 0-7, rows 8-15),
-  // turned into the two operands at use, with the non-temporal hint.
+  // Whole-line weight loads (rows 0-7, rows 8-15 of the tile over two 64-byte
+  // windows), turned into the two windows' operands at use, with the
+  // non-temporal hint. bf16 with two pieces per step: the two windows are the
+  // step's pieces (LINES). One piece per step (block-scaled, or bf16 C = 1):
+  // a ring slot holds two consecutive steps, one window each (PAIRS), and
+  // the slot's scale bytes come in one 8- (MXFP4) or 4-byte (MXFP8) load.
   constexpr bool LINES = !MX && C == 2;
-  constexpr int WPOL = LINES ? kPolicyStream : kPolicyDefault;
+  constexpr bool PAIRS = LOADS == 1;
+  constexpr int SLOT_K = PAIRS ? 2 * STEP_K : STEP_K;  // K elements of one ring slot
+  constexpr int RLOADS = PAIRS ? 2 : LOADS;            // 16-byte loads per lane per slot
+  constexpr int DR = PAIRS ? (D / 2 > 0 ? D / 2 : 1) : D;  // ring slots (same bytes in flight)
+  constexpr int WPOL = kPolicyStream;
   static_assert(WK == 1 || WN == 1, "waves that split a tile form one column");
   static_assert(!EPI || WK > 1, "an epilogue wave needs streaming waves");
 
@@ -411,8 +419,8 @@ void splitk_stream_kernel(GemmParams p) {
   const int col = gi * WN + wn;   // this wave column's first tile
   const int cstride = G * WN;     // distance between its tiles
   const int ntl = (col < n_tiles) ? (n_tiles - col + cstride - 1) / cstride : 0;
-  const int cs = p.ks / STEP_K;  // load steps per tile (whole slice)
-  const int n_i = epi_wave ? 0 : (cs - sw + SWK - 1) / SWK;  // this wave's steps per tile
+  const int cs = p.ks / SLOT_K;  // ring slots per tile (whole slice)
+  const int n_i = epi_wave ? 0 : (cs - sw + SWK - 1) / SWK;  // this wave's slots per tile
   const int total = ntl * n_i;
 
   const uint32_t wrow_bytes = row_bytes(WF, (uint32_t)K);
@@ -428,22 +436,28 @@ void splitk_stream_kernel(GemmParams p) {
 
   // ---- weight ring (streaming waves) -------------------------------------
   int pf_i = 0;
-  uint32_t pf_row = LINES ? (uint32_t)(col * 16) * wrow_bytes + line_pair_offset(li, 0, wrow_bytes)
-                          : (uint32_t)(col * 16 + li) * wrow_bytes;
-  uint32_t pf_srow = (uint32_t)(col * 16 + li) * (uint32_t)(K / 32);
+  uint32_t pf_row = (uint32_t)(col * 16) * wrow_bytes + line_pair_offset(li, 0, wrow_bytes);
+  uint32_t pf_srow = (uint32_t)(col * 16 + li) * (uint32_t)(K / 32);  // scales: operand layout
   const uint32_t row_step = (uint32_t)(cstride * 16) * wrow_bytes;
   const uint32_t srow_step = (uint32_t)(cstride * 16) * (uint32_t)(K / 32);
-  u32x4 ring[D][LOADS];
-  uint32_t sring[D];
+  u32x4 ring[DR][RLOADS];
+  u32x2 sring[DR];
   int issued = 0;
   auto issue = [&](int slot) {
     const bool ok = issued < total;
-    const int kel = kbase + (sw + SWK * pf_i) * STEP_K;
+    const int kel = kbase + (sw + SWK * pf_i) * SLOT_K;
     const uint32_t lo = elem_byte(WF, (uint32_t)kel) + 16u * g;
 #pragma unroll
-    for (int l = 0; l < LOADS; ++l)
-      ring[slot][l] = ld16_if<WPOL>(ok, wr, pf_row + lo + (LINES ? 8u * wrow_bytes : 64u) * l);
-    if constexpr (MX) sring[slot] = ld1_if(ok, sr, pf_srow + (uint32_t)((kel + LK * g) / 32));
+    for (int l = 0; l < RLOADS; ++l) ring[slot][l] = ld16_if<WPOL>(ok, wr, pf_row + lo + 8u * wrow_bytes * l);
+    if constexpr (MX) {
+      // The slot's 2 * STEP_K / 32 scale bytes of row li (8 for MXFP4, 4 for MXFP8).
+      const uint32_t so = pf_srow + (uint32_t)(kel / 32);
+      if constexpr (WF == kMxfp4) {
+        sring[slot] = ld8_if(ok, sr, so);
+      } else {
+        sring[slot] = u32x2{ld4_if(ok, sr, so), 0u};
+      }
+    }
     ++issued;
     if (++pf_i == n_i) {
       pf_i = 0;
@@ -509,7 +523,7 @@ void splitk_stream_kernel(GemmParams p) {
   __syncthreads();
   if (!epi_wave) {
 #pragma unroll
-    for (int s = 0; s < D; ++s) issue(s);
+    for (int s = 0; s < DR; ++s) issue(s);
   }
   stamp[1] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
 
@@ -613,33 +627,38 @@ void splitk_stream_kernel(GemmParams p) {
 #pragma unroll
   for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const u32x4 (&ld)[LOADS], uint32_t sc, int i) {
-    const int j = sw + SWK * i;
-    u32x4 a[LOADS];
-    if constexpr (LINES) {
-      line_pair_to_operands(ld[0], ld[1], a[0], a[1]);
-    } else {
+  // Slot i of this wave: windows w = 0, 1 of the line pair are load step
+  // 2 * js + w (PAIRS) or piece w of load step js (LINES), js = sw + SWK * i.
+  auto compute = [&](const u32x4 (&ld)[RLOADS], u32x2 sc, int i) {
+    const int js = sw + SWK * i;
+    u32x4 a[2];
+    line_pair_to_operands(ld[0], ld[1], a[0], a[1]);
 #pragma unroll
-      for (int l = 0; l < LOADS; ++l) a[l] = ld[l];
-    }
+    for (int w = 0; w < 2; ++w) {
+      const int j = PAIRS ? 2 * js + w : js;
 #pragma unroll
-    for (int s2 = 0; s2 < SUBS; ++s2) {
-      bf16x8 b[NT];
+      for (int s2 = 0; s2 < (PAIRS ? SUBS : 1); ++s2) {
+        const int sx = PAIRS ? s2 : w;  // sub-step index in the X layout
+        bf16x8 b[NT];
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        const int t = tt * 16 + li;
-        const bool ok = t < T;
-        const u32x4 v = lds_read16(smem, x_slot(j, s2, g, ok ? t : 0));
-        b[tt] = as_bf16x8(ok ? v : u32x4{0u, 0u, 0u, 0u});
+        for (int tt = 0; tt < NT; ++tt) {
+          const int t = tt * 16 + li;
+          const bool ok = t < T;
+          const u32x4 v = lds_read16(smem, x_slot(j, sx, g, ok ? t : 0));
+          b[tt] = as_bf16x8(ok ? v : u32x4{0u, 0u, 0u, 0u});
+        }
+        bf16x8 af;
+        if constexpr (MX) {
+          // Scale byte of (window w, lane block g) within the slot's bytes.
+          const int sb = (w * STEP_K + LK * g) / 32;
+          const uint32_t word = sb < 4 ? sc[0] : sc[1];
+          af = decode_operand<WF>(a[w], s2, e8m0_f32((word >> (8 * (sb & 3))) & 0xFFu));
+        } else {
+          af = as_bf16x8(a[w]);
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma_bf16(af, b[tt], acc[tt]);
       }
-      bf16x8 af;
-      if constexpr (MX) {
-        af = decode_operand<WF>(a[0], s2, e8m0_f32(sc));
-      } else {
-        af = as_bf16x8(a[s2]);
-      }
-#pragma unroll
-      for (int tt = 0; tt < NT; ++tt) acc[tt] = mfma_bf16(af, b[tt], acc[tt]);
     }
   };
 
@@ -690,9 +709,9 @@ void splitk_stream_kernel(GemmParams p) {
   };
 
   int q = 0;
-  for (; q + D <= total; q += D) {
+  for (; q + DR <= total; q += DR) {
 #pragma unroll
-    for (int s = 0; s < D; ++s) {
+    for (int s = 0; s < DR; ++s) {
       compute(ring[s], sring[s], c_i);
       issue(s);
       __builtin_amdgcn_sched_barrier(0);
@@ -700,7 +719,7 @@ void splitk_stream_kernel(GemmParams p) {
     }
   }
 #pragma unroll
-  for (int s = 0; s < D; ++s) {
+  for (int s = 0; s < DR; ++s) {
     if (q + s < total) {
       compute(ring[s], sring[s], c_i);
       consumed();
@@ -1017,11 +1036,12 @@ int env_int(const char* name, int dflt) {
 bool stream_fits(int si, int T, int N, int ks, int S, int wf, Tactic* t, int L = 1) {
   const StreamShape& c = kStreamShapes[si];
   if (t->nt > kStreamMaxNT || ks == 0) return false;
-  const int step = wf != kBf16 ? 4 * lane_k(wf) : 32 * c.c;
+  // K elements per ring slot: one step of two pieces, or two one-piece steps.
+  const int step = wf != kBf16 ? 2 * 4 * lane_k(wf) : 64;
   if (ks % step) return false;
   const int cs = ks / step;
   const int streaming = c.epi ? c.wk - 1 : c.wk;
-  if (cs < streaming) return false;  // every streaming wave needs a step per tile
+  if (cs < streaming) return false;  // every streaming wave needs a slot per tile
   const long x_lds = (long)T * ks * 2;
   if (x_lds > kStreamMaxX) return false;
   const int parked = c.epi ? c.wk - 1 : c.wk - 1;  // sums parked in LDS per tile
