@@ -43,6 +43,11 @@ namespace {
 
 constexpr int kClusterMaxRanks = 8;
 
+template <int V>
+struct ConstInt {
+  static constexpr int value = V;
+};
+
 // Load steps kept in flight per wave (operand registers: D * (C + NT*SUBS) * 4).
 constexpr int cluster_depth(int nt, int c, bool mx) {  // mx: block-scaled weights
   return mx ? (nt == 1 ? 4 : 2) : (nt == 1 ? (c == 2 ? 4 : 8) : (c == 2 ? 2 : 4));
@@ -248,44 +253,98 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
   const float* redf = reinterpret_cast<const float*>(red);
 
   // Pass 1: rank partial of (rank, token, row pair) = its waves' fold blocks,
-  // folds in order within a wave, waves in order.
+  // folds in order within a wave, waves in order. Pass 2: rank-order sum, one
+  // RNE rounding, one store per row pair. The split (S, hence waves per rank)
+  // is dispatched once to compile-time loop bounds, so both passes unroll.
   constexpr int PAIRS = R / 2;
   const int per_rank = PAIRS * T;
-  for (int o = tid; o < S * per_rank; o += 64 * WT) {
-    const int rk = o / per_rank;
-    const int rem = o - rk * per_rank;
-    const int t = rem / PAIRS;
-    const int r = (rem - t * PAIRS) * 2;
-    const int tt = t / 16;
-    const int tl = t - tt * 16;
-    float v0 = 0.f, v1 = 0.f;
-    for (int s = 0; s < WR; ++s) {
-      const float* wbase = redf + (size_t)(((rk * WR + s) * NT + tt) * 64) * 4;
+  // Folds 4 and 8 (T <= 4, short launches): runtime bounds keep the
+  // registers of the many fold blocks in check.
+  auto reduce_rt = [&]() {
+    for (int o = tid; o < S * per_rank; o += 64 * WT) {
+      const int rk = o / per_rank;
+      const int rem = o - rk * per_rank;
+      const int t = rem / PAIRS;
+      const int r = (rem - t * PAIRS) * 2;
+      const int tt = t / 16;
+      const int tl = t - tt * 16;
+      float v0 = 0.f, v1 = 0.f;
+      for (int s2 = 0; s2 < WR; ++s2) {
+        const float* wbase = redf + (size_t)(((rk * WR + s2) * NT + tt) * 64) * 4;
 #pragma unroll
-      for (int f = 0; f < F; ++f) {
-        const int row = f * R + r;  // rows row, row + 1 sit in one lane (R even)
-        const int col = f * TF + tl;
-        const float* e = wbase + (16 * (row >> 2) + col) * 4 + (row & 3);
-        v0 += e[0];
-        v1 += e[1];
+        for (int f = 0; f < F; ++f) {
+          const int row = f * R + r;
+          const int col = f * TF + tl;
+          const float* e = wbase + (16 * (row >> 2) + col) * 4 + (row & 3);
+          v0 += e[0];
+          v1 += e[1];
+        }
       }
+      part[(rk * 32 + t) * 16 + r] = v0;
+      part[(rk * 32 + t) * 16 + r + 1] = v1;
     }
-    part[(rk * 32 + t) * 16 + r] = v0;
-    part[(rk * 32 + t) * 16 + r + 1] = v1;
-  }
-  __syncthreads();
-
-  // Pass 2: rank-order sum, one RNE rounding, one store per row pair.
-  for (int o = tid; o < per_rank; o += 64 * WT) {
-    const int t = o / PAIRS;
-    const int r = (o - t * PAIRS) * 2;
-    float v0 = part[t * 16 + r];
-    float v1 = part[t * 16 + r + 1];
-    for (int rk = 1; rk < S; ++rk) {
-      v0 += part[(rk * 32 + t) * 16 + r];
-      v1 += part[(rk * 32 + t) * 16 + r + 1];
+    __syncthreads();
+    for (int o = tid; o < per_rank; o += 64 * WT) {
+      const int t = o / PAIRS;
+      const int r = (o - t * PAIRS) * 2;
+      float v0 = part[t * 16 + r];
+      float v1 = part[t * 16 + r + 1];
+      for (int rk = 1; rk < S; ++rk) {
+        v0 += part[(rk * 32 + t) * 16 + r];
+        v1 += part[(rk * 32 + t) * 16 + r + 1];
+      }
+      st4_if(true, bf16_pair(v0, v1), cr, ((uint32_t)t * (uint32_t)N + (uint32_t)(n0 + r)) * 2u);
     }
-    st4_if(true, bf16_pair(v0, v1), cr, ((uint32_t)t * (uint32_t)N + (uint32_t)(n0 + r)) * 2u);
+  };
+  auto reduce = [&](auto s_c) {
+    constexpr int SC = decltype(s_c)::value;
+    constexpr int WRC = WT / SC;
+    for (int o = tid; o < SC * per_rank; o += 64 * WT) {
+      const int rk = o / per_rank;
+      const int rem = o - rk * per_rank;
+      const int t = rem / PAIRS;
+      const int r = (rem - t * PAIRS) * 2;
+      const int tt = t / 16;
+      const int tl = t - tt * 16;
+      float v0 = 0.f, v1 = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < WRC; ++s2) {
+        const float* wbase = redf + (size_t)(((rk * WRC + s2) * NT + tt) * 64) * 4;
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+          const int row = f * R + r;  // rows row, row + 1 sit in one lane (R even)
+          const int col = f * TF + tl;
+          const float* e = wbase + (16 * (row >> 2) + col) * 4 + (row & 3);
+          v0 += e[0];
+          v1 += e[1];
+        }
+      }
+      part[(rk * 32 + t) * 16 + r] = v0;
+      part[(rk * 32 + t) * 16 + r + 1] = v1;
+    }
+    __syncthreads();
+    for (int o = tid; o < per_rank; o += 64 * WT) {
+      const int t = o / PAIRS;
+      const int r = (o - t * PAIRS) * 2;
+      float v0 = part[t * 16 + r];
+      float v1 = part[t * 16 + r + 1];
+#pragma unroll
+      for (int rk = 1; rk < SC; ++rk) {
+        v0 += part[(rk * 32 + t) * 16 + r];
+        v1 += part[(rk * 32 + t) * 16 + r + 1];
+      }
+      st4_if(true, bf16_pair(v0, v1), cr, ((uint32_t)t * (uint32_t)N + (uint32_t)(n0 + r)) * 2u);
+    }
+  };
+  if constexpr (F <= 2) {
+    switch (S) {  // S divides WT (the host keeps S | WT), S <= 8
+      case 1: reduce(ConstInt<1>{}); break;
+      case 2: reduce(ConstInt<(WT >= 2 ? 2 : 1)>{}); break;
+      case 4: reduce(ConstInt<(WT >= 4 ? 4 : 1)>{}); break;
+      default: reduce(ConstInt<(WT >= 8 ? 8 : 1)>{}); break;
+    }
+  } else {
+    reduce_rt();
   }
   // Thread 0 writes the stamps (vector stores): entry, loads issued, wave 0's
   // stream done, all waves' sums in LDS, exit.
