@@ -24,12 +24,16 @@
 //
 // Operands come straight from memory into registers: weights with 16-byte
 // buffer loads (C pieces per lane, D steps in flight per wave), and
-// activations the same way from X, which every workgroup reads and so stays
-// in L2. Lanes of tokens t >= T take an out-of-range offset and read zeros
-// with no memory access (page vllm.models.muse_spark.amd.mono.kernels.dev,
-// ld_vec_if). MXFP4 lanes load 16 bytes = 32 E2M1 codes = one scale block
-// and decode them into four bf16x8 operands (same page, fp4x8_bf16 and
-// e8m0_f32).
+// activations from X, which every workgroup reads and so stays in L2. Lanes
+// of tokens t >= T take an out-of-range offset and read zeros with no memory
+// access (page vllm.models.muse_spark.amd.mono.kernels.dev, ld_vec_if).
+// MXFP4 lanes load 16 bytes = 32 E2M1 codes = one scale block and decode
+// them into four bf16x8 operands (same page, fp4x8_bf16 and e8m0_f32).
+// Load layouts: weight loads cover whole 128-byte lines (folded tiles
+// natively, unfolded bf16 tiles as row 0-7 / 8-15 line pairs), with the
+// non-temporal hint; for folds 1 and 2, activation loads read contiguous runs
+// and are moved to their operand lanes with ds_bpermute (block-scaled pieces
+// are transposed across lane rows to match). See the notes at each.
 
 #include "device/mfma.h"
 #include "device/pack.h"
@@ -42,6 +46,7 @@ namespace skg {
 namespace {
 
 constexpr int kClusterMaxRanks = 8;
+constexpr int kClusterMaxWaves = 8;
 
 template <int V>
 struct ConstInt {
@@ -372,7 +377,6 @@ hipError_t launch_cluster_wt(const Tactic& t, const GemmParams& p, hipStream_t s
   switch (t.wk) {
     case 4: return launch_cluster_one<NT, F, 4, C, WF>(t, p, s);
     case 8: return launch_cluster_one<NT, F, 8, C, WF>(t, p, s);
-    case 16: return launch_cluster_one<NT, F, 16, C, WF>(t, p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -409,18 +413,13 @@ bool cluster_fits(int T, int N, int ks, int S, int wf, int max_fold, int force_c
   // K=7168, N=4096: 16-row tiles 16.3 us, 8-row tiles 21.8 us).
   while (fold > 1 && (long)(N / (32 / fold)) * L >= kChipCUs) fold /= 2;
   if (fold > max_fold) fold = max_fold;
-  // Pieces per lane (bf16): two unless the tile is folded and one piece per
-  // lane still gives every wave at least four load steps (measured K=7168,
-  // S=4, T=5..8: 7.5-9.6 us with one piece against 8.4-10.7 us with two;
-  // K=2048, S=2: 5.9 against 5.5 us). Unfolded tiles keep two, which their
-  // whole-line load pairs need.
+  // Pieces per lane (bf16): two unless the tile is folded and its rank
+  // slices hold at least 64 / S one-piece steps each (S * steps >= 64;
+  // measured K=7168, S=4, T=5..8: 7.7-9.8 us with one piece against
+  // 8.3-10.6 us with two; K=2048, S=2 (32 steps): 5.9 against 5.5 us).
+  // Unfolded tiles keep two, which their whole-line load pairs need.
   int c_first = 2;
-  if (!mx && fold >= 2 && ks % (fold * 32) == 0) {
-    const int cs1 = ks / (fold * 32);
-    int wt1 = 4;
-    while (wt1 < (S * cs1 < 16 ? S * cs1 : 16)) wt1 *= 2;
-    if (wt1 >= S && cs1 / (wt1 / S) >= 4) c_first = 1;
-  }
+  if (!mx && fold >= 2 && ks % (fold * 32) == 0 && S * (ks / (fold * 32)) >= 64) c_first = 1;
   for (int ci = 0; ci < 2; ++ci) {
     const int c = ci == 0 ? c_first : 3 - c_first;
     if (mx && c == 2) continue;  // one 16-byte MXFP4 piece is a whole step
@@ -429,9 +428,12 @@ bool cluster_fits(int T, int N, int ks, int S, int wf, int max_fold, int force_c
       const int step = f * (mx ? 4 * lane_k(wf) : 32 * c);
       if (ks % step) continue;
       const int cs = ks / step;
-      // Waves: a power of two in 4..16, at least S (so S divides it), and
-      // no more per rank group than the slice has steps.
-      const int want = S * cs < 16 ? S * cs : 16;
+      // Waves: a power of two in 4..8, at least S (so S divides it), and
+      // no more per rank group than the slice has steps. Eight waves with
+      // twice the steps each beat sixteen (measured T=16 K=7168 N=4096:
+      // MXFP4 11.7 -> 10.8 us, MXFP8 14.6 -> 14.1 us; bf16 T=8: 8.45 ->
+      // 8.37 us at N=2048, 13.7 -> 13.5 us at N=4096).
+      const int want = S * cs < kClusterMaxWaves ? S * cs : kClusterMaxWaves;
       int wt = 4;
       while (wt < want) wt *= 2;
       if (wt < S) continue;
