@@ -130,3 +130,32 @@ def test_tactics_cover_the_workloads(T, N, K, S, mx):
     step = 128 if mx else 32
     assert t["kc"] % step == 0
     assert min(T, 128) * t["kc"] * 2 <= 128 * 1024
+
+
+# The kernel choices the tactic makes, each fixed by a measurement on MI355X
+# (cold weights, graph replay): folded cluster tiles take one piece per lane
+# when S * (one-piece steps per rank slice) >= 64; the cluster fold shrinks
+# while the grid still covers the 256 CUs; an unfolded cluster grid below 256
+# workgroups gives way to the persistent kernel; a single problem runs the
+# persistent kernel at one workgroup per CU; cluster workgroups have at most
+# eight waves.
+@pytest.mark.parametrize("T,N,K,S,wf,want", [
+    (8, 2048, 7168, 4, 0, {"kind": "cluster", "fold": 2, "c": 1, "wk": 8, "grid": 256}),
+    (8, 1024, 2048, 2, 0, {"kind": "cluster", "fold": 2, "c": 2}),
+    (8, 4096, 7168, 4, 0, {"kind": "cluster", "fold": 1, "c": 2, "grid": 256}),
+    (5, 1024, 7168, 4, 0, {"kind": "cluster", "fold": 2, "grid": 128}),
+    (1, 1024, 1024, 4, 0, {"kind": "cluster", "fold": 4, "c": 2, "grid": 256}),
+    (16, 4096, 7168, 4, 1, {"kind": "cluster", "fold": 1, "wk": 8}),
+    (16, 4096, 7168, 4, 2, {"kind": "cluster", "fold": 1, "wk": 8}),
+    (12, 1024, 7168, 4, 0, {"kind": "stream", "grid": 256}),
+    (32, 2048, 7168, 4, 0, {"kind": "stream", "grid": 256}),
+    (32, 18432, 7168, 8, 0, {"kind": "stream", "grid": 256}),
+    (64, 16384, 16384, 4, 0, {"kind": "wide"}),
+])
+def test_tactic_rules(T, N, K, S, wf, want):
+    _ensure_built()
+    t = sk.skgemm_tactic_for(T, N, K, S, wf)
+    got = {k: t[k] for k in want}
+    assert got == want, (T, N, K, S, wf, t)
+    if t["kind"] == "cluster":
+        assert t["wk"] <= 8
