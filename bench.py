@@ -455,6 +455,49 @@ def pmc_summary(path: str, name: str = HEADLINE) -> dict:
     return out
 
 
+def mfma_summary(path: str, name: str = HEADLINE) -> dict:
+    """Matrix-core use of a workload's kernel from one ``--pmc MfmaUtil
+    MfmaFlopsBF16`` pass of ``--pmc-run`` under ``path`` (rocprofv3's derived
+    counters: MFMA busy cycles over all SIMDs / (GPU active cycles x SIMDs),
+    and BF16 MFMA operations x 512), per dispatch, averaged over the
+    workload's launches."""
+    import csv
+
+    rows = []
+    for f in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            rows += [r for r in csv.DictReader(fh) if "splitk_" in r.get("Kernel_Name", "")]
+    if not rows:
+        raise SystemExit(f"no GEMM counter rows under {path}")
+    val = {}
+    kernels = sorted({r["Kernel_Name"] for r in rows})
+    for counter in ("MfmaUtil", "MfmaFlopsBF16"):
+        v = [float(r["Counter_Value"]) for r in rows if r.get("Counter_Name") == counter]
+        if len(v) != PMC_LAUNCHES or len(kernels) != 1:
+            raise SystemExit(f"{counter}: {len(v)} GEMM dispatches of {kernels}")
+        val[counter] = float(np.mean(v))
+    wl = workloads.get(name)
+    flops = wl.flops()
+    out = {
+        "workload": name,
+        "kernel": kernels[0].split("(")[0].replace("void ", ""),
+        "kernel_source_sha": kernel_source_hash(),
+        "mfma_util_percent": round(val["MfmaUtil"], 2),
+        "mfma_flops_bf16_per_launch": int(round(val["MfmaFlopsBF16"])),
+        "algorithmic_flops_per_launch": flops,
+        "executed_over_algorithmic": round(val["MfmaFlopsBF16"] / flops, 3),
+        "commands": [
+            "cd /tmp && timeout -s KILL 150 rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv "
+            f"-d $R/gpurun_out/mfma_{name} -o mfma -- python3 $R/bench.py --pmc-run {name}",
+            f"python bench.py --mfma-summary gpurun_out/mfma_{name} {name}",
+        ],
+        "note": ("R is the repository root. Executed MFMA flops exceed 2*T*N*K by the token padding to "
+                 "16 and, in folded tiles, by the off-diagonal blocks that are computed and not read."),
+    }
+    print(json.dumps(out, indent=1))
+    return out
+
+
 # ---------------------------------------------------------------------------
 
 
@@ -481,11 +524,16 @@ def main() -> None:
     ap.add_argument("--trace-summary", metavar="DIR", help="summarise a rocprofv3 kernel trace and exit")
     ap.add_argument("--pmc-run", nargs="?", const=HEADLINE, metavar="WORKLOAD",
                     help="the short run HBM counters are taken on (default: the headline)")
+    ap.add_argument("--mfma-summary", nargs="+", metavar=("DIR", "WORKLOAD"),
+                    help="summarise an MfmaUtil / MfmaFlopsBF16 counter pass of --pmc-run and exit")
     ap.add_argument("--pmc-summary", nargs="+", metavar=("DIR", "WORKLOAD"),
                     help="summarise rocprofv3 counter CSVs under DIR (for WORKLOAD) and exit")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary[:2])
+        return
+    if args.mfma_summary:
+        mfma_summary(*args.mfma_summary[:2])
         return
     if args.pmc_run:
         pmc_run(args.pmc_run)
