@@ -9,9 +9,12 @@
 // meets a 16-token activation tile in each v_mfma_f32_16x16x32_bf16.
 //
 // MI355X design, one workgroup = (output tile of TILE_N features, split rank):
-//  * Weight stream: every lane issues 16-byte buffer loads with the streaming
-//    (NT) policy straight into MFMA A operands -- the role of the pages'
-//    evict-first weight TMA (SplitKGemm.weight_warp, _tma_load_evict_first).
+//  * Weight stream: every lane issues 16-byte buffer loads straight into
+//    MFMA A operands -- the role of the pages' evict-first weight TMA
+//    (SplitKGemm.weight_warp, _tma_load_evict_first). The persistent kernel
+//    loads whole-line pairs with the non-temporal hint (the closer analogue
+//    of evict-first); the one-tile-per-workgroup fallback loads operands
+//    directly with the default policy.
 //    D load steps per row group stay in flight, all issued before any use
 //    (page vllm.models.deepseek_v41.amd.mono.common.ops, batched_rounds).
 //    Past the end a load takes an out-of-range offset and returns zeros
@@ -339,9 +342,11 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
 //
 // grid = S * G workgroups; workgroup (gi, rank) owns K slice `rank` and stages
 // that slice of X in LDS once, shared by all its waves for all its tiles.
-// Weights stream through one D-deep register ring per wave that runs on
-// across tile boundaries, so neither the staging nor the load latency is
-// paid per tile. Three organisations of the waves:
+// Weights stream through one register ring per wave that runs on across
+// tile boundaries, so neither the staging nor the load latency is paid per
+// tile; each ring slot is a whole-line load pair (rows 0-7 and 8-15 over two
+// 64-byte windows, non-temporal), rearranged into MFMA operands at use.
+// Three organisations of the waves:
 //
 // * WK > 1, EPI = 0: all WK waves stream, splitting every tile's K slice
 //   (interleaved load steps). At a tile's end they meet in LDS; wave 0 adds
