@@ -124,7 +124,8 @@ int ensure_workspace(hipStream_t stream, size_t part_bytes, size_t cnt_count, Wo
 size_t part_bytes_for(int T, int N, int S) {
   return (size_t)S * (size_t)std::min(T, kTokenBlock) * (size_t)N * sizeof(float);
 }
-size_t counters_for(int N) { return (size_t)N / 16; }
+// Arrival counters, one per 16 output rows, kCntStride words apart.
+size_t counters_for(int N) { return (size_t)N / 16 * skg::kCntStride; }
 
 // Compute units of the current device (the owner wait is used only while the
 // whole grid fits on them).

@@ -13,7 +13,7 @@ struct GemmParams {
   const void* x;          // bf16 [T, K]
   void* c;                // bf16 [T, N]
   float* part;            // FP32 partials [S, T, N] (S > 1)
-  uint32_t* cnt;          // one arrival counter per output tile (S > 1)
+  uint32_t* cnt;          // arrival counters, one per 16-row group, kCntStride words apart (S > 1)
   int T, N, K, S;
   int ks;       // K / S: the K slice of one split rank
   int kc;       // K elements of X staged in LDS at a time; divides ks
@@ -30,6 +30,11 @@ struct GemmParams {
   uint64_t bpart;            // floats between problems' partials
   uint32_t bcnt;             // counters between problems' counters
 };
+
+// Words between the split-K arrival counters of two 16-row groups (one
+// 128-byte line per counter: the S ranks' arrivals and an owner's polls of
+// one tile then meet no other tile's at the device-scope atomic units).
+constexpr int kCntStride = 32;
 
 // Health words of a workspace: word 0 counts owner waits that ran out of time
 // (the tile then went to the last rank to arrive); words 8 + 8r .. 8 + 8r + 4

@@ -271,7 +271,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
 
   constexpr uint32_t kArrivals = 0xFFu;
   constexpr uint32_t kAbandon = 0x100u;
-  uint32_t* cnt = p.cnt + (n0 / 16 + wn * RG);
+  uint32_t* cnt = p.cnt + (size_t)(n0 / 16 + wn * RG) * kCntStride;  // one 128-byte line each
   const bool owner = (wn + tile) % S == rank;
   uint32_t old = 0;
   if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
