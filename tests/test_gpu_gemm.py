@@ -470,6 +470,23 @@ def test_wide_integer_exact(S, monkeypatch):
         assert np.array_equal(F.bf16_bits_to_f64(run_bf16(x, w, S)), F.bf16_bits_to_f64(want))
 
 
+def test_kinds_share_counters(monkeypatch):
+    """The persistent, wide and tiled kernels hand off through the same
+    arrival-counter area of one stream's workspace (one counter line per 16
+    output rows). Interleaved twice over one N, every launch must return its
+    counters to zero for the next kind: bit-exact results on integer operands."""
+    N, K, S = 1024, 4096, 8
+    runs = [("1", 32), ("3", 64), ("0", 32), ("1", 8), ("0", 80), ("3", 128)]
+    for rep in range(2):
+        for kind, T in runs:
+            monkeypatch.setenv("SKGEMM_KIND", kind)
+            tac = sk.skgemm_tactic_for(T, N, K, S)
+            log(f"shared counters rep={rep} kind={kind} T={T} N={N} K={K} S={S} tactic={tac}")
+            x, w = workloads.integer_bf16_case(T, K, N, seed=9300 + 10 * rep + T, mag=2)
+            want = F.f32_to_bf16_rne(G.gemm_bf16_ref(x, w).astype(np.float32))
+            assert np.array_equal(F.bf16_bits_to_f64(run_bf16(x, w, S)), F.bf16_bits_to_f64(want))
+
+
 BATCH_KINDS = [("2", [(3, 512, 1024, 4), (16, 256, 2048, 2)]),   # cluster
                ("1", [(8, 2048, 4096, 4), (24, 1024, 2048, 8)]),  # stream
                ("3", [(40, 512, 4096, 4), (128, 256, 2048, 2)]),  # wide
