@@ -146,7 +146,8 @@ SKGEMM_API int skgemm_mxfp8_batched(const void* Wq8, const void* Wscale, const v
  * and split_k <= max_split_k. Call it before capturing a stream into a HIP
  * graph: inside a capture the workspace can not grow (SKGEMM_ENOMEM). The
  * workspace is FP32 partials [split_k, min(T,128), N] and one uint32 counter
- * per output tile; counters return to zero at the end of every call.
+ * per 16 output rows, each on a 128-byte line of its own; counters return to
+ * zero at the end of every call.
  * May synchronise `stream` when it replaces a smaller workspace.
  */
 SKGEMM_API int skgemm_reserve(int max_T, int max_N, int max_split_k, hipStream_t stream);
@@ -159,7 +160,8 @@ SKGEMM_API int skgemm_reserve_batched(int max_T, int max_N, int max_split_k, int
                                       hipStream_t stream);
 
 /* skgemm_release: free every workspace of the calling process. Synchronises
- * the device first. Not to be called while other threads enqueue work. */
+ * each workspace's device first and restores the calling thread's current
+ * device afterwards. Not to be called while other threads enqueue work. */
 SKGEMM_API int skgemm_release(void);
 
 /*

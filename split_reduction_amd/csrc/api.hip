@@ -283,6 +283,10 @@ SKGEMM_API int skgemm_reserve_batched(int max_T, int max_N, int max_split_k, int
 SKGEMM_API int skgemm_release(void) {
   std::lock_guard<std::mutex> lock(g_ws_mu);
   int rc = SKGEMM_OK;
+  // Each workspace is freed with its own device current; the caller's
+  // current device is restored afterwards.
+  int caller_dev = -1;
+  if (hipGetDevice(&caller_dev) != hipSuccess) caller_dev = -1;
   for (auto& kv : g_ws) {
     hipError_t e = hipSetDevice(kv.first.first);
     if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -291,6 +295,10 @@ SKGEMM_API int skgemm_release(void) {
     if (kv.second.cnt) (void)hipFree(kv.second.cnt);
   }
   g_ws.clear();
+  if (caller_dev >= 0) {
+    const hipError_t e = hipSetDevice(caller_dev);
+    if (e != hipSuccess && rc == SKGEMM_OK) rc = hip_fail(e);
+  }
   return rc;
 }
 
