@@ -59,6 +59,17 @@ constexpr int stream_waves_per_eu(int nt, int waves) {
   return (stream_wgs_per_cu(nt) * waves + 3) / 4 > 0 ? (stream_wgs_per_cu(nt) * waves + 3) / 4 : 1;
 }
 
+// Organisations of the stream kernel's waves (template MODE).
+constexpr int kStreamDeferred = 0;  // every wave streams; wave 0 also stores each tile's partial
+constexpr int kStreamEpilogue = 1;  // wave 0 sums, stores and hands off each tile (pipelined)
+constexpr int kStreamStorer = 2;    // wave 0 only sums and stores; deferred hand-off at the end
+
+// Register budget: resident waves per SIMD. The storer organisation runs one
+// workgroup per CU (single problems).
+constexpr int stream_mode_waves_per_eu(int nt, int waves, int mode) {
+  return mode == kStreamStorer ? (waves + 3) / 4 : stream_waves_per_eu(nt, waves);
+}
+
 __device__ __forceinline__ u32x4 lds_read16(const uint8_t* smem, int slot) {
   return *reinterpret_cast<const u32x4*>(smem + slot * 16);
 }
@@ -346,33 +357,43 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
 // tile boundaries, so neither the staging nor the load latency is paid per
 // tile; each ring slot is a whole-line load pair (rows 0-7 and 8-15 over two
 // 64-byte windows, non-temporal), rearranged into MFMA operands at use.
-// Three organisations of the waves:
+// Organisations of the waves (MODE):
 //
-// * WK > 1, EPI = 0: all WK waves stream, splitting every tile's K slice
+// * Deferred, WK > 1: all WK waves stream, splitting every tile's K slice
 //   (interleaved load steps). At a tile's end they meet in LDS; wave 0 adds
 //   the others' sums in wave order (the pages' row_sum) and stores the tile's
 //   FP32 partial (device-coherent) or, without a split, the bf16 output.
-// * WK > 1, EPI = 1: wave 0 is a dedicated epilogue wave (the pages'
+// * Storer, WK > 1: as deferred, but wave 0 does not stream: waves 1..WK-1
+//   park their sums and wave 0 adds them in wave order and stores. Its
+//   stores then share no completion counter with a weight ring: a
+//   device-coherent store is acknowledged late, and a streaming wave that
+//   issued one stalls on it at its next ring wait (measured: without
+//   mid-stream stores T=32 K=7168 N=18432 runs 59 instead of 65 us).
+// * Epilogue, WK > 1: wave 0 is a dedicated epilogue wave (the pages'
 //   SplitKGemm keeps weight, MMA and epilogue roles in separate warps) and
 //   waves 1..WK-1 stream. The epilogue wave sums the parked partials in wave
 //   order and runs the split-K hand-off as a per-tile pipeline: store the
 //   partial, one tile later bump the tile's counter, one tile later load the
 //   ranks' partials if it arrived last, one tile later sum them in rank order
 //   and store C, waiting only for its own operations of the previous stage.
-// * WK == 1: each of the WN waves streams its own tiles (column gi*WN + wn
-//   takes tiles gi*WN + wn, + G*WN, ...) and stores its own partials.
+// * WK == 1 (deferred): each of the WN waves streams its own tiles (column
+//   gi*WN + wn takes tiles gi*WN + wn, + G*WN, ...) and stores its own
+//   partials.
 //
 // Without an epilogue wave the hand-off is deferred to the workgroup's end:
-// loads and stores share one completion counter and may complete out of order
-// relative to each other, so waiting for a store mid-stream would drain the
-// ring. At the end each wave takes every WK-th tile: one vector atomic bumps
-// all their counters (a lane per tile) and the tiles it arrived last on are
-// finished two at a time, all partial loads in flight before the sums.
-template <int NT, int WK, int WN, int D, int C, bool EPI, int WF>
+// loads and stores share one completion counter, so waiting for a store
+// mid-stream would drain the ring. At the end each wave takes every WK-th
+// tile: one vector atomic bumps all their counters (a lane per tile) and the
+// tiles it arrived last on are finished two at a time, all partial loads in
+// flight before the sums.
+template <int NT, int WK, int WN, int D, int C, int MODE, int WF>
 __global__ __launch_bounds__(64 * WK * WN)
-__attribute__((amdgpu_waves_per_eu(stream_waves_per_eu(NT, WK * WN))))
+__attribute__((amdgpu_waves_per_eu(stream_mode_waves_per_eu(NT, WK * WN, MODE))))
 void splitk_stream_kernel(GemmParams p) {
   select_problem(p);
+  constexpr bool EPI = MODE == kStreamEpilogue;
+  constexpr bool STORER = MODE == kStreamStorer;
+  constexpr bool SIDE = EPI || STORER;  // wave 0 is a side wave that does not stream
   constexpr bool MX = WF != kBf16;  // block-scaled weights
   constexpr int LK = lane_k(WF);     // K elements of one lane's 16-byte piece
   constexpr int THREADS = 64 * WK * WN;
@@ -380,8 +401,8 @@ void splitk_stream_kernel(GemmParams p) {
   constexpr int SUBS = MX ? LK / 8 : C;
   constexpr int STEP_K = MX ? 4 * LK : 32 * C;
   constexpr int XBATCH = 4;
-  constexpr int SWK = EPI ? WK - 1 : WK;   // streaming waves per tile
-  constexpr int PARKED = EPI ? SWK : WK - 1;  // partial sums parked in LDS per tile
+  constexpr int SWK = SIDE ? WK - 1 : WK;   // streaming waves per tile
+  constexpr int PARKED = SIDE ? SWK : WK - 1;  // partial sums parked in LDS per tile
   constexpr int RED_QUADS = (PARKED > 0 ? PARKED : 1) * NT * 64;  // one parity half
   // Whole-line weight loads (rows 0-7, rows 8-15 of the tile over two 64-byte
   // windows), turned into the two windows' operands at use, with the
@@ -396,7 +417,7 @@ void splitk_stream_kernel(GemmParams p) {
   constexpr int DR = PAIRS ? (D / 2 > 0 ? D / 2 : 1) : D;  // ring slots (same bytes in flight)
   constexpr int WPOL = kPolicyStream;
   static_assert(WK == 1 || WN == 1, "waves that split a tile form one column");
-  static_assert(!EPI || WK > 1, "an epilogue wave needs streaming waves");
+  static_assert(!SIDE || (WK > 1 && WN == 1), "a side wave serves one column of streaming waves");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
@@ -409,8 +430,8 @@ void splitk_stream_kernel(GemmParams p) {
   const int wn = wave / WK;
   const int g = lane >> 4;
   const int li = lane & 15;
-  const bool epi_wave = EPI && wave == 0;
-  const int sw = EPI ? wk - 1 : wk;  // index among the streaming waves of the tile
+  const bool epi_wave = SIDE && wave == 0;  // the side wave (epilogue or storer)
+  const int sw = SIDE ? wk - 1 : wk;  // index among the streaming waves of the tile
 
   const int S = p.S;
   const int T = p.T;
@@ -676,7 +697,7 @@ void splitk_stream_kernel(GemmParams p) {
     const int tile = col + cstride * k;
     f32x4* red = red_base + (k & 1) * RED_QUADS;
     bool storer = true;
-    if constexpr (EPI) {
+    if constexpr (SIDE) {
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) red[(sw * NT + tt) * 64 + lane] = acc[tt];
       __syncthreads();
@@ -734,10 +755,36 @@ void splitk_stream_kernel(GemmParams p) {
       consumed();
     }
   }
-  // A streaming wave with no steps (slice shorter than the wave count)
-  // still takes part in every tile's barrier.
   if (n_i == 0) {
-    for (int k = 0; k < ntl; ++k) tile_end(k);
+    if (STORER && epi_wave) {
+      // The storer wave: per tile, the streaming waves' sums in wave order,
+      // then the tile's partial (or, with one rank, C) stored. It never
+      // waits for its stores before the end, so their acknowledgements hold
+      // up no weight load.
+      for (int k = 0; k < ntl; ++k) {
+        __syncthreads();  // tile k's sums are in LDS
+        const int tile = col + cstride * k;
+        const f32x4* red = red_base + (k & 1) * RED_QUADS;
+        f32x4 sum[NT];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) sum[tt] = red[tt * 64 + lane];
+#pragma unroll 1
+        for (int w = 1; w < SWK; ++w)
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) sum[tt] += red[(w * NT + tt) * 64 + lane];
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) {
+          if (S == 1)
+            st8_if(in_t(tt), bf16_quad(sum[tt]), cr, c_off(tile, tt));
+          else
+            st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, sum[tt]), pr, p_off(rank, tile, tt));
+        }
+      }
+    } else {
+      // A streaming wave with no steps (slice shorter than the wave count)
+      // still takes part in every tile's barrier.
+      for (int k = 0; k < ntl; ++k) tile_end(k);
+    }
   }
   stamp[2] = stamp[3] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
   if (EPI || S == 1) {
@@ -990,15 +1037,16 @@ bool shape_fits(int si, int T, int N, int ks, int S, int wf, Tactic* t) {
 // ---- persistent stream kernel configurations --------------------------
 
 struct StreamShape {
-  int wk, wn, d, c, epi;
+  int wk, wn, d, c, mode;
 };
 constexpr StreamShape kStreamShapes[] = {
-    {8, 1, 8, 2, 0},  // 0: 8 waves share each tile's K slice, deferred hand-off
-    {8, 1, 8, 1, 0},  // 1
-    {8, 1, 8, 2, 1},  // 2: 7 streaming waves + an epilogue wave (pipelined hand-off)
-    {8, 1, 8, 1, 1},  // 3
-    {4, 1, 8, 1, 0},  // 4
-    {1, 8, 8, 2, 0},  // 5: 8 waves, each streaming its own tiles
+    {8, 1, 8, 2, kStreamDeferred},  // 0: 8 waves share each tile's K slice, deferred hand-off
+    {8, 1, 8, 1, kStreamDeferred},  // 1
+    {8, 1, 8, 2, kStreamEpilogue},  // 2: 7 streaming waves + an epilogue wave (pipelined hand-off)
+    {8, 1, 8, 1, kStreamEpilogue},  // 3
+    {4, 1, 8, 1, kStreamDeferred},  // 4
+    {1, 8, 8, 2, kStreamDeferred},  // 5: 8 waves, each streaming its own tiles
+    {8, 1, 8, 2, kStreamStorer},    // 6: 7 streaming waves + a storer wave
 };
 constexpr int kNumStreamShapes = sizeof(kStreamShapes) / sizeof(kStreamShapes[0]);
 constexpr int kStreamMaxNT = 2;
@@ -1009,7 +1057,7 @@ constexpr long kClusterMaxBatchGrid = 8192;
 template <int NT, int SH, int WF>
 hipError_t launch_stream_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
   constexpr StreamShape sh = kStreamShapes[SH];
-  auto kern = splitk_stream_kernel<NT, sh.wk, sh.wn, sh.d, sh.c, sh.epi != 0, WF>;
+  auto kern = splitk_stream_kernel<NT, sh.wk, sh.wn, sh.d, sh.c, sh.mode, WF>;
   hipLaunchKernelGGL(kern, dim3(t.grid, p.L), dim3(t.threads), t.lds, s, p);
   return hipGetLastError();
 }
@@ -1023,6 +1071,7 @@ hipError_t launch_stream_nt(int sh, const Tactic& t, const GemmParams& p, hipStr
     case 3: return launch_stream_one<NT, 3, WF>(t, p, s);
     case 4: return launch_stream_one<NT, 4, WF>(t, p, s);
     case 5: return launch_stream_one<NT, 5, WF>(t, p, s);
+    case 6: return launch_stream_one<NT, 6, WF>(t, p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1049,11 +1098,13 @@ bool stream_fits(int si, int T, int N, int ks, int S, int wf, Tactic* t, int L =
   const int step = wf != kBf16 ? 2 * 4 * lane_k(wf) : 64;
   if (ks % step) return false;
   const int cs = ks / step;
-  const int streaming = c.epi ? c.wk - 1 : c.wk;
+  const int streaming = c.mode == kStreamDeferred ? c.wk : c.wk - 1;
   if (cs < streaming) return false;  // every streaming wave needs a slot per tile
+  // The storer organisation is built for one workgroup per CU (single problems).
+  if (c.mode == kStreamStorer && L != 1) return false;
   const long x_lds = (long)T * ks * 2;
   if (x_lds > kStreamMaxX) return false;
-  const int parked = c.epi ? c.wk - 1 : c.wk - 1;  // sums parked in LDS per tile
+  const int parked = c.wk - 1;  // sums parked in LDS per tile
   const int red = c.wk > 1 ? 2 * parked * t->nt * 64 * 16 : 0;
   const long lds = x_lds + red;
   if (lds > kMaxLds) return false;
@@ -1143,10 +1194,21 @@ bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L) {
       // With few tiles per workgroup the hand-off is most of the tail, and a
       // dedicated epilogue wave that overlaps it with the stream wins; with
       // many tiles all eight waves streaming wins.
-      static const int many[] = {0, 1, 2, 3, 4, 5};
-      static const int few[] = {2, 3, 0, 1, 4, 5};
+      // Where a tile's ring slots split evenly over 7 waves and not over 8
+      // (single problems), 7 streaming waves and a storer wave, which keeps
+      // the partial stores out of the streaming waves (measured T=32 K=7168
+      // N=18432, 14 slots: 63.0-63.5 against 65.1-65.2 us; neutral where 8
+      // waves split the slots evenly, K=N=16384 T=1..32).
+      const int step = wf != kBf16 ? 2 * 4 * lane_k(wf) : 64;
+      const int cs = ks / step;
+      const bool by7 = cs % 8 != 0 && cs % 7 == 0;
+      static const int many8[] = {0, 1, 2, 3, 4, 5, 6};
+      static const int many7[] = {6, 0, 1, 2, 3, 4, 5};
+      static const int few[] = {2, 3, 0, 1, 4, 5, 6};
+      const int* many = by7 ? many7 : many8;
       const int* pref = many;
-      for (int si : many) {
+      for (int mi = 0; mi < kNumStreamShapes; ++mi) {
+        const int si = many[mi];
         Tactic probe = t;
         if (stream_fits(si, tr, N, ks, S, wf, &probe, L)) {
           const int groups = probe.grid / S;

@@ -309,7 +309,7 @@ def test_graph_replays_match_eager():
 # it off, SKGEMM_SHAPE a one-tile-per-workgroup shape), on shapes with ragged
 # T, uneven step counts per wave and several tiles per wave column.
 FORCED = (
-    [{"SKGEMM_KIND": "1", "SKGEMM_STREAM": str(i)} for i in range(6)]
+    [{"SKGEMM_KIND": "1", "SKGEMM_STREAM": str(i)} for i in range(7)]
     + [{"SKGEMM_KIND": "0", "SKGEMM_SHAPE": str(i)} for i in range(6)]
     + [{"SKGEMM_KIND": "2", "SKGEMM_FOLD": str(f), "SKGEMM_CLUSTER_C": str(c)}
        for f in (1, 2, 4, 8) for c in (1, 2)]
@@ -388,7 +388,7 @@ def test_cluster_integer_exact(monkeypatch):
                 f"fold<={f} T={T} S={S}"
 
 
-@pytest.mark.parametrize("shape", ["1", "4", "5"])
+@pytest.mark.parametrize("shape", ["1", "4", "5", "6"])
 @pytest.mark.parametrize("wait", ["0", "1", "10000"])
 def test_owner_handover(wait, shape, monkeypatch):
     """The persistent kernel's tile owners wait as usual, give up at once, or
