@@ -196,6 +196,7 @@ int run_gemm(int wf, const void* w, const void* ws, const void* x, void* c, int 
     const bool all_resident =
         tac.resident > 0 && cus > 0 && (long)tac.grid * L <= (long)cus * tac.resident;
     p.owner_wait = all_resident ? owner_wait_ticks() : 0u;
+    p.pdefer = tac.pdefer;
     p.health = wsp.cnt != nullptr ? wsp.cnt + wsp.cnt_count : nullptr;
     p.L = L;
     p.bw = batch.bw;
@@ -362,10 +363,10 @@ SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int weight_fo
              "{\"nt\": %d, \"rg\": %d, \"wk\": %d, \"wn\": %d, \"d\": %d, \"c\": %d, \"kc\": %d, "
              "\"tile_n\": %d, \"threads\": %d, \"lds\": %d, \"grid\": %d, \"split_k\": %d, "
              "\"token_blocks\": %d, \"mxfp4\": %d, \"weight_format\": %d, \"kind\": \"%s\", "
-             "\"shape\": %d, \"fold\": %d}",
+             "\"shape\": %d, \"fold\": %d, \"pdefer\": %d}",
              t.nt, t.rg, t.wk, t.wn, t.d, t.c, t.kc, t.tile_n, t.threads, t.lds, t.grid, split_k,
              blocks, t.wf == skg::kMxfp4 ? 1 : 0, t.wf, t.kind == 3 ? "wide" : t.kind == 2 ? "cluster" : (t.kind == 1 ? "stream" : "tiled"), t.shape,
-             t.kind == 2 ? t.fold : 1);
+             t.kind == 2 ? t.fold : 1, t.pdefer);
   }
   return SKGEMM_OK;
 }

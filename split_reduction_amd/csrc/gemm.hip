@@ -463,6 +463,9 @@ void splitk_stream_kernel(GemmParams p) {
   // X slot of (load step j, sub-step s, lane K block gg, token t): compact tile.
   auto x_slot = [&](int j, int s, int gg, int t) -> int { return ((j * SUBS + s) * 4 + gg) * T + t; };
   f32x4* red_base = reinterpret_cast<f32x4*>(smem + (size_t)T * p.ks * 2);  // 16-byte aligned
+  // With p.pdefer, tile k's FP32 partial waits in LDS (after the reduction
+  // buffers) until the stream ends: NT * 64 quads per tile.
+  f32x4* pbuf = red_base + (WK > 1 ? 2 * RED_QUADS : 0);
 
   // ---- weight ring (streaming waves) -------------------------------------
   int pf_i = 0;
@@ -721,6 +724,8 @@ void splitk_stream_kernel(GemmParams p) {
       for (int tt = 0; tt < NT; ++tt) {
         if (S == 1)
           st8_if(in_t(tt), bf16_quad(acc[tt]), cr, c_off(tile, tt));
+        else if (p.pdefer)
+          pbuf[(k * NT + tt) * 64 + lane] = acc[tt];
         else
           st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, acc[tt]), pr, p_off(rank, tile, tt));
       }
@@ -776,6 +781,8 @@ void splitk_stream_kernel(GemmParams p) {
         for (int tt = 0; tt < NT; ++tt) {
           if (S == 1)
             st8_if(in_t(tt), bf16_quad(sum[tt]), cr, c_off(tile, tt));
+          else if (p.pdefer)
+            pbuf[(k * NT + tt) * 64 + lane] = sum[tt];
           else
             st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, sum[tt]), pr, p_off(rank, tile, tt));
         }
@@ -802,6 +809,20 @@ void splitk_stream_kernel(GemmParams p) {
   // peer that is not resident, e.g. under a concurrent kernel), the owner sets
   // the abandon bit and the last rank to arrive finishes the tile instead, so
   // the result never depends on the peers being resident.
+  if (p.pdefer) {
+    // The partials held in LDS go out now, in one burst after the stream,
+    // the workgroup's waves taking every WK-th tile (measured: mid-stream
+    // partial stores slow the weight stream itself, T=32 K=7168 N=18432
+    // 55-57 us without them against 63-65 us with).
+    __syncthreads();  // every tile's partial is in LDS
+    for (int k = wk; k < ntl; k += WK) {
+      const int tile = col + cstride * k;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+        st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, pbuf[(k * NT + tt) * 64 + lane]), pr,
+                         p_off(rank, tile, tt));
+    }
+  }
   wait_vmem_all();  // this wave's partial stores are complete (coherent)
   if (p.stamps) stamp[3] = __builtin_amdgcn_s_memrealtime();
   int k0 = 0, kstep = 1;
@@ -1137,6 +1158,18 @@ bool stream_fits(int si, int T, int N, int ks, int S, int wf, Tactic* t, int L =
   t->grid = (int)g * S;
   t->shape = si;
   t->resident = per_cu;
+  // Partials held in LDS until the stream ends, where they fit beside the
+  // activation slice (single problems, waves sharing each tile, split K).
+  t->pdefer = 0;
+  if (L == 1 && S > 1 && c.wk > 1 && c.wn == 1 && c.mode != kStreamEpilogue &&
+      env_int("SKGEMM_PDEFER", 1) != 0) {
+    const long per_wg = (n_tiles + g - 1) / g;  // tiles of the busiest workgroup
+    const long pl = per_wg * t->nt * 64 * 16;
+    if (lds + pl <= kMaxLds) {
+      t->pdefer = 1;
+      t->lds = (int)(lds + pl);
+    }
+  }
   return true;
 }
 

@@ -23,6 +23,8 @@ struct GemmParams {
   uint32_t owner_wait;  // device-clock ticks (100 MHz) a tile's owner waits for
                         // the other ranks before handing the tile to the last
                         // to arrive (0: hand over at once)
+  int pdefer;  // stream kernel: partials held in LDS until the stream ends (1) or
+               // stored tile by tile (0)
   // A batch of independent problems of one shape (grid.y = L): problem l
   // reads and writes at these strides from the pointers above.
   int L;
@@ -95,6 +97,7 @@ struct Tactic {
   int shape;    // index into the kind's shape table
   int fold;     // kind 2: K windows folded into one MFMA operand (tile rows 16/fold)
   int resident; // workgroups per CU the grid sizing counts on (0: none assumed)
+  int pdefer;   // kind 1: partials held in LDS until the stream ends
 };
 
 // Picks the configuration for a launch over T <= 128 rows of weight format wf

@@ -470,6 +470,29 @@ def test_wide_integer_exact(S, monkeypatch):
         assert np.array_equal(F.bf16_bits_to_f64(run_bf16(x, w, S)), F.bf16_bits_to_f64(want))
 
 
+def test_partials_held_in_lds_bit_identical(monkeypatch):
+    """The persistent kernel holds tile partials in LDS until its stream ends
+    where they fit (pdefer) and stores them tile by tile otherwise: the same
+    sums in the same order, so both give identical bits, and both meet the
+    oracle's bound (deferred and storer organisations, one and two token
+    tiles)."""
+    cases = [(32, 2304, 7168, 8), (16, 4096, 4096, 8), (8, 8192, 8192, 4), (5, 4096, 4096, 8)]
+    for (T, N, K, S) in cases:
+        x, w = workloads.small_bf16_case(T, K, N, seed=9400 + T + S)
+        ref = G.gemm_bf16_ref(x, w)
+        W = to_dev_bf16(w)
+        got = {}
+        for flag in ("1", "0"):
+            monkeypatch.setenv("SKGEMM_KIND", "1")
+            monkeypatch.setenv("SKGEMM_PDEFER", flag)
+            tac = sk.skgemm_tactic_for(T, N, K, S)
+            log(f"pdefer={flag}: T={T} N={N} K={K} S={S} tactic={tac}")
+            assert tac["kind"] == "stream" and tac["pdefer"] == int(flag)
+            got[flag] = run_bf16(x, None, S, W=W)
+            assert_parity(got[flag], ref, K, f"pdefer={flag} T={T} S={S}")
+        assert np.array_equal(got["1"], got["0"])
+
+
 def test_kinds_share_counters(monkeypatch):
     """The persistent, wide and tiled kernels hand off through the same
     arrival-counter area of one stream's workspace (one counter line per 16
