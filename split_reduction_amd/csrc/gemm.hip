@@ -765,26 +765,52 @@ void splitk_stream_kernel(GemmParams p) {
       // The storer wave: per tile, the streaming waves' sums in wave order,
       // then the tile's partial (or, with one rank, C) stored. It never
       // waits for its stores before the end, so their acknowledgements hold
-      // up no weight load.
-      for (int k = 0; k < ntl; ++k) {
-        __syncthreads();  // tile k's sums are in LDS
-        const int tile = col + cstride * k;
+      // up no weight load. Split partials that are not held in LDS are held
+      // in this wave's registers (it has no weight ring) and stored HOLD
+      // tiles at a time, in bursts rather than tile by tile.
+      constexpr int HOLD = 16;
+      auto tile_sum = [&](int k, f32x4 (&sum)[NT]) {
         const f32x4* red = red_base + (k & 1) * RED_QUADS;
-        f32x4 sum[NT];
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt) sum[tt] = red[tt * 64 + lane];
 #pragma unroll 1
         for (int w = 1; w < SWK; ++w)
 #pragma unroll
           for (int tt = 0; tt < NT; ++tt) sum[tt] += red[(w * NT + tt) * 64 + lane];
+      };
+      if (S > 1 && !p.pdefer) {
+        for (int k0 = 0; k0 < ntl; k0 += HOLD) {
+          f32x4 hold[HOLD][NT];
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-          if (S == 1)
-            st8_if(in_t(tt), bf16_quad(sum[tt]), cr, c_off(tile, tt));
-          else if (p.pdefer)
-            pbuf[(k * NT + tt) * 64 + lane] = sum[tt];
-          else
-            st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, sum[tt]), pr, p_off(rank, tile, tt));
+          for (int j = 0; j < HOLD; ++j) {
+            if (k0 + j < ntl) {
+              __syncthreads();  // tile k0 + j's sums are in LDS
+              tile_sum(k0 + j, hold[j]);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < HOLD; ++j) {
+            if (k0 + j < ntl) {
+              const int tile = col + cstride * (k0 + j);
+#pragma unroll
+              for (int tt = 0; tt < NT; ++tt)
+                st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, hold[j][tt]), pr, p_off(rank, tile, tt));
+            }
+          }
+        }
+      } else {
+        for (int k = 0; k < ntl; ++k) {
+          __syncthreads();  // tile k's sums are in LDS
+          const int tile = col + cstride * k;
+          f32x4 sum[NT];
+          tile_sum(k, sum);
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) {
+            if (S == 1)
+              st8_if(in_t(tt), bf16_quad(sum[tt]), cr, c_off(tile, tt));
+            else
+              pbuf[(k * NT + tt) * 64 + lane] = sum[tt];
+          }
         }
       }
     } else {
@@ -1240,6 +1266,7 @@ bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L) {
       static const int few[] = {2, 3, 0, 1, 4, 5, 6};
       const int* many = by7 ? many7 : many8;
       const int* pref = many;
+      bool held = true;  // the preferred shape holds its partials in LDS (or needs none)
       for (int mi = 0; mi < kNumStreamShapes; ++mi) {
         const int si = many[mi];
         Tactic probe = t;
@@ -1247,8 +1274,15 @@ bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L) {
           const int groups = probe.grid / S;
           const int per_wg = (N / 16 + groups - 1) / groups;
           if (per_wg <= 4) pref = few;
+          held = S == 1 || probe.pdefer != 0;
           break;
         }
+      }
+      // Where the partials do not fit in LDS, the storer wave holds them in
+      // its registers and stores them in bursts (K=N=16384 T=24/32).
+      if (pref == many && !held && stream_fits(6, tr, N, ks, S, wf, &t, L)) {
+        *out = t;
+        return true;
       }
       for (int oi = 0; oi < kNumStreamShapes; ++oi) {
         const int si = pref[oi];

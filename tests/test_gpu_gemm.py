@@ -470,26 +470,30 @@ def test_wide_integer_exact(S, monkeypatch):
         assert np.array_equal(F.bf16_bits_to_f64(run_bf16(x, w, S)), F.bf16_bits_to_f64(want))
 
 
-def test_partials_held_in_lds_bit_identical(monkeypatch):
+@pytest.mark.parametrize("shape", ["0", "6"])
+def test_partials_held_in_lds_bit_identical(shape, monkeypatch):
     """The persistent kernel holds tile partials in LDS until its stream ends
-    where they fit (pdefer) and stores them tile by tile otherwise: the same
-    sums in the same order, so both give identical bits, and both meet the
-    oracle's bound (deferred and storer organisations, one and two token
-    tiles)."""
-    cases = [(32, 2304, 7168, 8), (16, 4096, 4096, 8), (8, 8192, 8192, 4), (5, 4096, 4096, 8)]
+    where they fit (pdefer); otherwise it stores them tile by tile (deferred
+    organisation, shape 0) or from the storer wave's registers in bursts
+    (shape 6). The same sums in the same order: identical bits either way,
+    and both meet the oracle's bound (one and two token tiles, S = 4 and 8)."""
+    # (the last: 1029 tiles over 32 workgroups, 32-33 each: register batches of 16, 16 and 1)
+    cases = [(32, 2304, 7168, 8), (16, 4096, 4096, 8), (8, 8192, 8192, 4), (5, 4096, 4096, 8),
+             (12, 16464, 4096, 8)]
+    monkeypatch.setenv("SKGEMM_KIND", "1")
+    monkeypatch.setenv("SKGEMM_STREAM", shape)
     for (T, N, K, S) in cases:
         x, w = workloads.small_bf16_case(T, K, N, seed=9400 + T + S)
         ref = G.gemm_bf16_ref(x, w)
         W = to_dev_bf16(w)
         got = {}
         for flag in ("1", "0"):
-            monkeypatch.setenv("SKGEMM_KIND", "1")
             monkeypatch.setenv("SKGEMM_PDEFER", flag)
             tac = sk.skgemm_tactic_for(T, N, K, S)
-            log(f"pdefer={flag}: T={T} N={N} K={K} S={S} tactic={tac}")
-            assert tac["kind"] == "stream" and tac["pdefer"] == int(flag)
+            log(f"shape {shape} pdefer={flag}: T={T} N={N} K={K} S={S} tactic={tac}")
+            assert tac["kind"] == "stream" and tac["shape"] == int(shape) and tac["pdefer"] == int(flag)
             got[flag] = run_bf16(x, None, S, W=W)
-            assert_parity(got[flag], ref, K, f"pdefer={flag} T={T} S={S}")
+            assert_parity(got[flag], ref, K, f"shape {shape} pdefer={flag} T={T} S={S}")
         assert np.array_equal(got["1"], got["0"])
 
 
