@@ -835,14 +835,18 @@ void splitk_stream_kernel(GemmParams p) {
   // peer that is not resident, e.g. under a concurrent kernel), the owner sets
   // the abandon bit and the last rank to arrive finishes the tile instead, so
   // the result never depends on the peers being resident.
+  auto tile_at = [&](int k) { return col + cstride * k; };
+  auto owner_of = [&](int k) { return (k + gi) % S; };
   if (p.pdefer) {
     // The partials held in LDS go out now, in one burst after the stream,
     // the workgroup's waves taking every WK-th tile (measured: mid-stream
     // partial stores slow the weight stream itself, T=32 K=7168 N=18432
-    // 55-57 us without them against 63-65 us with).
+    // 55-57 us without them against 63-65 us with). Tiles this rank owns
+    // stay in LDS: their owner sums them from there.
     __syncthreads();  // every tile's partial is in LDS
     for (int k = wk; k < ntl; k += WK) {
-      const int tile = col + cstride * k;
+      if (owner_of(k) == rank) continue;
+      const int tile = tile_at(k);
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
         st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, pbuf[(k * NT + tt) * 64 + lane]), pr,
@@ -859,22 +863,30 @@ void splitk_stream_kernel(GemmParams p) {
   }
   constexpr uint32_t kArrivals = 0xFFu;  // arrival count bits of a counter
   constexpr uint32_t kAbandon = 0x100u;  // the owner stopped waiting
-  auto tile_at = [&](int k) { return col + cstride * k; };
-  auto owner_of = [&](int k) { return (k + gi) % S; };
 
-  // Sums the S partials of tile t0 (and t1 >= 0) in rank order, one store.
-  auto finish = [&](int t0, int t1) {
-    const int t1c = t1 >= 0 ? t1 : t0;
+  // Sums the S partials of the tiles at list positions k0i (and k1i >= 0) in
+  // rank order, one store each. With `held`, this rank's own partial is
+  // taken from LDS (the owner's, which was never stored).
+  auto finish = [&](int k0i, int k1i, bool held) {
+    const int t0 = tile_at(k0i);
+    const int t1c = k1i >= 0 ? tile_at(k1i) : t0;
+    const int h0 = k0i;
+    const int h1 = k1i >= 0 ? k1i : k0i;
 #pragma unroll 1
     for (int tt = 0; tt < NT; ++tt) {
       const bool ok = in_t(tt);
-      const bool ok1 = ok && t1 >= 0;
+      const bool ok1 = ok && k1i >= 0;
       f32x4 v0[8], v1[8];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         if (r < S) {
-          v0[r] = __builtin_bit_cast(f32x4, ld16_coherent_if(ok, pr, p_off(r, t0, tt)));
-          v1[r] = __builtin_bit_cast(f32x4, ld16_coherent_if(ok1, pr, p_off(r, t1c, tt)));
+          const bool own = held && r == rank;
+          v0[r] = __builtin_bit_cast(f32x4, ld16_coherent_if(ok && !own, pr, p_off(r, t0, tt)));
+          v1[r] = __builtin_bit_cast(f32x4, ld16_coherent_if(ok1 && !own, pr, p_off(r, t1c, tt)));
+          if (own) {
+            v0[r] = pbuf[(h0 * NT + tt) * 64 + lane];
+            v1[r] = pbuf[(h1 * NT + tt) * 64 + lane];
+          }
         }
       }
       f32x4 s0 = v0[0], s1 = v1[0];
@@ -889,14 +901,15 @@ void splitk_stream_kernel(GemmParams p) {
       st8_if(ok1, bf16_quad(s1), cr, c_off(t1c, tt));
     }
   };
-  // Finishes the tiles of the lanes set in `mask`, two at a time.
-  auto finish_mask = [&](uint64_t mask, auto tile_of_lane) {
+  // Finishes the tiles of the lanes set in `mask` (list position of lane b:
+  // pos_of_lane(b)), two at a time.
+  auto finish_mask = [&](uint64_t mask, auto pos_of_lane, bool held) {
     while (mask) {
       const int b0 = __builtin_ctzll(mask);
       mask &= mask - 1;
       const int b1 = mask ? __builtin_ctzll(mask) : -1;
       if (b1 >= 0) mask &= mask - 1;
-      finish(tile_of_lane(b0), b1 >= 0 ? tile_of_lane(b1) : -1);
+      finish(pos_of_lane(b0), b1 >= 0 ? pos_of_lane(b1) : -1, held);
     }
   };
 
@@ -914,8 +927,7 @@ void splitk_stream_kernel(GemmParams p) {
       take = owner_of(k) != rank && (old & kAbandon) != 0 && (old & kArrivals) == (uint32_t)(S - 1);
       if (take) __hip_atomic_store(cnt_of(tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    finish_mask(__builtin_amdgcn_ballot_w64(take),
-                [&](int b) { return tile_at(k0 + kstep * (j0 + b)); });
+    finish_mask(__builtin_amdgcn_ballot_w64(take), [&](int b) { return k0 + kstep * (j0 + b); }, false);
   }
 
   // Owned tiles: k = k_first + S*m, m spread over the waves like the list.
@@ -940,6 +952,21 @@ void splitk_stream_kernel(GemmParams p) {
       }
       if (__builtin_amdgcn_ballot_w64(pending) == 0) break;
       if (__builtin_amdgcn_s_memrealtime() > deadline) {
+        if (p.pdefer) {
+          // The tile may go to another rank now: its partial from this rank,
+          // held in LDS so far, is stored (and complete) before the abandon.
+          uint64_t pm = __builtin_amdgcn_ballot_w64(pending);
+          while (pm) {
+            const int b = __builtin_ctzll(pm);
+            pm &= pm - 1;
+            const int kk = own_k(i0 + b);
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+              st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, pbuf[(kk * NT + tt) * 64 + lane]), pr,
+                               p_off(rank, tile_at(kk), tt));
+          }
+          wait_vmem_all();
+        }
         if (pending) {
           const uint32_t old = __hip_atomic_fetch_or(cnt_of(tile), kAbandon, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
@@ -952,7 +979,7 @@ void splitk_stream_kernel(GemmParams p) {
       __builtin_amdgcn_s_sleep(2);
     }
     if (ready) __hip_atomic_store(cnt_of(tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    finish_mask(__builtin_amdgcn_ballot_w64(ready), [&](int b) { return tile_at(own_k(i0 + b)); });
+    finish_mask(__builtin_amdgcn_ballot_w64(ready), [&](int b) { return own_k(i0 + b); }, p.pdefer != 0);
   }
   write_stamps();
 }
