@@ -1280,18 +1280,16 @@ bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L) {
       // With few tiles per workgroup the hand-off is most of the tail, and a
       // dedicated epilogue wave that overlaps it with the stream wins; with
       // many tiles all eight waves streaming wins.
-      // Where a tile's ring slots split evenly over 7 waves and not over 8
-      // (single problems), 7 streaming waves and a storer wave, which keeps
-      // the partial stores out of the streaming waves (measured T=32 K=7168
-      // N=18432, 14 slots: 63.0-63.5 against 65.1-65.2 us; neutral where 8
-      // waves split the slots evenly, K=N=16384 T=1..32).
-      const int step = wf != kBf16 ? 2 * 4 * lane_k(wf) : 64;
-      const int cs = ks / step;
-      const bool by7 = cs % 8 != 0 && cs % 7 == 0;
-      static const int many8[] = {0, 1, 2, 3, 4, 5, 6};
-      static const int many7[] = {6, 0, 1, 2, 3, 4, 5};
+      // Single problems with many tiles per workgroup: 7 streaming waves and
+      // a storer wave, which takes each tile's wave-order sum and its partial
+      // off the streaming waves (measured with partials held in LDS:
+      // K=N=16384 T=1 / 8 / 16 85.0-85.6 / 87.2-88.3 / 89.9-90.3 us against
+      // 87.3-87.8 / 89.4-89.7 / 91.3 us with 8 streaming waves; T=32
+      // K=7168 N=18432 57.3 against 62.2-62.5 us). Where the storer shape
+      // does not fit (batches, slices of fewer than 7 ring slots per tile),
+      // 8 streaming waves.
+      static const int many[] = {6, 0, 1, 2, 3, 4, 5};
       static const int few[] = {2, 3, 0, 1, 4, 5, 6};
-      const int* many = by7 ? many7 : many8;
       const int* pref = many;
       bool held = true;  // the preferred shape holds its partials in LDS (or needs none)
       for (int mi = 0; mi < kNumStreamShapes; ++mi) {

@@ -138,11 +138,11 @@ def test_tactics_cover_the_workloads(T, N, K, S, mx):
 # while the grid still covers the 256 CUs; an unfolded cluster grid below 256
 # workgroups gives way to the persistent kernel; a single problem runs the
 # persistent kernel at one workgroup per CU; cluster workgroups have at most
-# eight waves. Persistent organisation: a storer wave (shape 6) where a
-# tile's 14 ring slots split evenly over 7 waves (K=7168, S=8) and where the
-# partials do not fit in LDS (K=N=16384 T=24/32, held in the storer's
-# registers); partials held in LDS until the stream ends wherever they fit
-# (pdefer); the epilogue-wave shape (2) for few tiles per workgroup.
+# eight waves. Persistent organisation: 7 streaming waves and a storer wave
+# (shape 6) for single problems with many tiles per workgroup, the partials
+# held in LDS until the stream ends wherever they fit (pdefer) and in the
+# storer's registers where they do not (K=N=16384 T=24/32); the
+# epilogue-wave shape (2) for few tiles per workgroup.
 @pytest.mark.parametrize("T,N,K,S,wf,want", [
     (8, 2048, 7168, 4, 0, {"kind": "cluster", "fold": 2, "c": 1, "wk": 8, "grid": 256}),
     (8, 1024, 2048, 2, 0, {"kind": "cluster", "fold": 2, "c": 2}),
@@ -154,8 +154,8 @@ def test_tactics_cover_the_workloads(T, N, K, S, mx):
     (12, 1024, 7168, 4, 0, {"kind": "stream", "grid": 256}),
     (32, 2048, 7168, 4, 0, {"kind": "stream", "grid": 256}),
     (32, 18432, 7168, 8, 0, {"kind": "stream", "grid": 256, "shape": 6, "pdefer": 1}),
-    (8, 16384, 16384, 8, 0, {"kind": "stream", "shape": 0, "pdefer": 1}),
-    (16, 16384, 16384, 8, 0, {"kind": "stream", "shape": 0, "pdefer": 1}),
+    (8, 16384, 16384, 8, 0, {"kind": "stream", "shape": 6, "pdefer": 1}),
+    (16, 16384, 16384, 8, 0, {"kind": "stream", "shape": 6, "pdefer": 1}),
     (24, 16384, 16384, 8, 0, {"kind": "stream", "shape": 6, "pdefer": 0}),
     (32, 16384, 16384, 8, 0, {"kind": "stream", "shape": 6, "pdefer": 0}),
     (12, 1024, 7168, 4, 0, {"kind": "stream", "shape": 2, "pdefer": 0}),
