@@ -102,12 +102,43 @@ def _check(code: int, name: str) -> None:
         raise SkgemmError(code, f"{name}: {strerror(code)}{extra}")
 
 
-def _ptr(a) -> int:
+def _ptr(a, nbytes: int = 0, what: str = "argument") -> int:
+    """Device address of a tensor or of a plain integer address (None is 0).
+
+    A tensor must live on the GPU, be contiguous and hold at least `nbytes`
+    from its first element: the kernels read or write that dense block at the
+    address, so a host tensor, a strided view or a short buffer would reach the
+    device as a bad address. Such tensors raise SkgemmError(SKGEMM_EINVAL) here,
+    before anything is launched. Integer addresses are passed through unchecked
+    (the caller vouches for them)."""
     if a is None:
         return 0
     if isinstance(a, int):
         return a
+    if a.device.type != "cuda":
+        raise SkgemmError(SKGEMM_EINVAL, f"{what}: a tensor on {a.device}, not on the GPU")
+    if not a.is_contiguous():
+        raise SkgemmError(SKGEMM_EINVAL, f"{what}: not contiguous")
+    have = a.numel() * a.element_size()
+    if have < nbytes:
+        raise SkgemmError(SKGEMM_EINVAL, f"{what}: holds {have} bytes, the call needs {nbytes}")
     return a.data_ptr()
+
+
+def _n(*dims) -> int:
+    """Product of the sizes, 0 if any is not positive (the library rejects or
+    skips such calls itself, so they need no bytes)."""
+    out = 1
+    for d in dims:
+        if d <= 0:
+            return 0
+        out *= d
+    return out
+
+
+def _batched(L: int, stride: int, one: int) -> int:
+    """Bytes spanned by L problems `stride` bytes apart, each `one` bytes."""
+    return 0 if L <= 0 or one == 0 else (L - 1) * max(stride, 0) + one
 
 
 def _stream(stream) -> int:
@@ -122,13 +153,15 @@ def _stream(stream) -> int:
 
 def skgemm_bf16(W, X, C, T: int, N: int, K: int, split_k: int, stream=None) -> None:
     """C[T, N] = X[T, K] . W[N, K]^T (bf16 in and out, FP32 accumulation)."""
-    code = lib().skgemm_bf16(_ptr(W), _ptr(X), _ptr(C), T, N, K, split_k, _stream(stream))
+    code = lib().skgemm_bf16(_ptr(W, 2 * _n(N, K), "W"), _ptr(X, 2 * _n(T, K), "X"),
+                             _ptr(C, 2 * _n(T, N), "C"), T, N, K, split_k, _stream(stream))
     _check(code, "skgemm_bf16")
 
 
 def skgemm_mxfp4(Wq, Wscale, X, C, T: int, N: int, K: int, split_k: int, stream=None) -> None:
     """C = X . dequant(Wq, Wscale)^T with MXFP4 weights decoded in registers."""
-    code = lib().skgemm_mxfp4(_ptr(Wq), _ptr(Wscale), _ptr(X), _ptr(C), T, N, K, split_k,
+    code = lib().skgemm_mxfp4(_ptr(Wq, _n(N, K) // 2, "Wq"), _ptr(Wscale, _n(N, K) // 32, "Wscale"),
+                              _ptr(X, 2 * _n(T, K), "X"), _ptr(C, 2 * _n(T, N), "C"), T, N, K, split_k,
                               _stream(stream))
     _check(code, "skgemm_mxfp4")
 
@@ -136,35 +169,48 @@ def skgemm_mxfp4(Wq, Wscale, X, C, T: int, N: int, K: int, split_k: int, stream=
 def skgemm_bf16_batched(W, X, C, T: int, N: int, K: int, split_k: int, L: int, w_stride: int,
                         x_stride: int, c_stride: int, stream=None) -> None:
     """L problems of one shape in one launch; strides in bytes."""
-    code = lib().skgemm_bf16_batched(_ptr(W), _ptr(X), _ptr(C), T, N, K, split_k, L, w_stride, x_stride,
-                                     c_stride, _stream(stream))
+    code = lib().skgemm_bf16_batched(_ptr(W, _batched(L, w_stride, 2 * _n(N, K)), "W"),
+                                     _ptr(X, _batched(L, x_stride, 2 * _n(T, K)), "X"),
+                                     _ptr(C, _batched(L, c_stride, 2 * _n(T, N)), "C"),
+                                     T, N, K, split_k, L, w_stride, x_stride, c_stride, _stream(stream))
     _check(code, "skgemm_bf16_batched")
 
 
 def skgemm_mxfp4_batched(Wq, Wscale, X, C, T: int, N: int, K: int, split_k: int, L: int, wq_stride: int,
                          wscale_stride: int, x_stride: int, c_stride: int, stream=None) -> None:
     """L MXFP4 problems of one shape in one launch; strides in bytes."""
-    code = lib().skgemm_mxfp4_batched(_ptr(Wq), _ptr(Wscale), _ptr(X), _ptr(C), T, N, K, split_k, L,
-                                      wq_stride, wscale_stride, x_stride, c_stride, _stream(stream))
+    code = lib().skgemm_mxfp4_batched(_ptr(Wq, _batched(L, wq_stride, _n(N, K) // 2), "Wq"),
+                                      _ptr(Wscale, _batched(L, wscale_stride, _n(N, K) // 32), "Wscale"),
+                                      _ptr(X, _batched(L, x_stride, 2 * _n(T, K)), "X"),
+                                      _ptr(C, _batched(L, c_stride, 2 * _n(T, N)), "C"),
+                                      T, N, K, split_k, L, wq_stride, wscale_stride, x_stride, c_stride,
+                                      _stream(stream))
     _check(code, "skgemm_mxfp4_batched")
 
 
 def skgemm_mxfp8(Wq8, Wscale, X, C, T: int, N: int, K: int, split_k: int, stream=None) -> None:
     """C = X . dequant(Wq8, Wscale)^T with E4M3 weights and E8M0 block scales."""
-    code = lib().skgemm_mxfp8(_ptr(Wq8), _ptr(Wscale), _ptr(X), _ptr(C), T, N, K, split_k, _stream(stream))
+    code = lib().skgemm_mxfp8(_ptr(Wq8, _n(N, K), "Wq8"), _ptr(Wscale, _n(N, K) // 32, "Wscale"),
+                              _ptr(X, 2 * _n(T, K), "X"), _ptr(C, 2 * _n(T, N), "C"), T, N, K, split_k,
+                              _stream(stream))
     _check(code, "skgemm_mxfp8")
 
 
 def skgemm_mxfp8_batched(Wq8, Wscale, X, C, T: int, N: int, K: int, split_k: int, L: int, wq8_stride: int,
                          wscale_stride: int, x_stride: int, c_stride: int, stream=None) -> None:
     """L MXFP8 problems of one shape in one launch; strides in bytes."""
-    code = lib().skgemm_mxfp8_batched(_ptr(Wq8), _ptr(Wscale), _ptr(X), _ptr(C), T, N, K, split_k, L,
-                                      wq8_stride, wscale_stride, x_stride, c_stride, _stream(stream))
+    code = lib().skgemm_mxfp8_batched(_ptr(Wq8, _batched(L, wq8_stride, _n(N, K)), "Wq8"),
+                                      _ptr(Wscale, _batched(L, wscale_stride, _n(N, K) // 32), "Wscale"),
+                                      _ptr(X, _batched(L, x_stride, 2 * _n(T, K)), "X"),
+                                      _ptr(C, _batched(L, c_stride, 2 * _n(T, N)), "C"),
+                                      T, N, K, split_k, L, wq8_stride, wscale_stride, x_stride, c_stride,
+                                      _stream(stream))
     _check(code, "skgemm_mxfp8_batched")
 
 
 def skgemm_mxfp8_dequant(Wq8, Wscale, W_out, N: int, K: int, stream=None) -> None:
-    code = lib().skgemm_mxfp8_dequant(_ptr(Wq8), _ptr(Wscale), _ptr(W_out), N, K, _stream(stream))
+    code = lib().skgemm_mxfp8_dequant(_ptr(Wq8, _n(N, K), "Wq8"), _ptr(Wscale, _n(N, K) // 32, "Wscale"),
+                                      _ptr(W_out, 2 * _n(N, K), "W_out"), N, K, _stream(stream))
     _check(code, "skgemm_mxfp8_dequant")
 
 
@@ -182,20 +228,24 @@ def skgemm_release() -> None:
 
 
 def skgemm_mxfp4_dequant(Wq, Wscale, W_out, N: int, K: int, stream=None) -> None:
-    code = lib().skgemm_mxfp4_dequant(_ptr(Wq), _ptr(Wscale), _ptr(W_out), N, K, _stream(stream))
+    code = lib().skgemm_mxfp4_dequant(_ptr(Wq, _n(N, K) // 2, "Wq"), _ptr(Wscale, _n(N, K) // 32, "Wscale"),
+                                      _ptr(W_out, 2 * _n(N, K), "W_out"), N, K, _stream(stream))
     _check(code, "skgemm_mxfp4_dequant")
 
 
 def skgemm_pack_bf16(inp, out, n_pairs: int, stream=None) -> None:
-    _check(lib().skgemm_pack_bf16(_ptr(inp), _ptr(out), n_pairs, _stream(stream)), "skgemm_pack_bf16")
+    _check(lib().skgemm_pack_bf16(_ptr(inp, 8 * n_pairs, "in"), _ptr(out, 4 * n_pairs, "out"), n_pairs,
+                                  _stream(stream)), "skgemm_pack_bf16")
 
 
 def skgemm_pack_e4m3(inp, out, n_quads: int, stream=None) -> None:
-    _check(lib().skgemm_pack_e4m3(_ptr(inp), _ptr(out), n_quads, _stream(stream)), "skgemm_pack_e4m3")
+    _check(lib().skgemm_pack_e4m3(_ptr(inp, 16 * n_quads, "in"), _ptr(out, 4 * n_quads, "out"), n_quads,
+                                  _stream(stream)), "skgemm_pack_e4m3")
 
 
 def skgemm_wave_sum(inp, out, n_waves: int, stream=None) -> None:
-    _check(lib().skgemm_wave_sum(_ptr(inp), _ptr(out), n_waves, _stream(stream)), "skgemm_wave_sum")
+    _check(lib().skgemm_wave_sum(_ptr(inp, 256 * n_waves, "in"), _ptr(out, 256 * n_waves, "out"), n_waves,
+                                 _stream(stream)), "skgemm_wave_sum")
 
 
 def skgemm_tactic_for(T: int, N: int, K: int, split_k: int, weight_format: int = 0) -> dict:
@@ -209,12 +259,14 @@ def skgemm_tactic_for(T: int, N: int, K: int, split_k: int, weight_format: int =
 
 def skgemm_set_timeline(buf, capacity: int) -> None:
     """Opt-in per-workgroup phase stamps of the stream kernel (None turns them off)."""
-    _check(lib().skgemm_set_timeline(_ptr(buf), capacity if buf is not None else 0), "skgemm_set_timeline")
+    _check(lib().skgemm_set_timeline(_ptr(buf, 8 * capacity if buf is not None else 0, "buf"),
+                                     capacity if buf is not None else 0), "skgemm_set_timeline")
 
 
 def skgemm_read_probe(src, nbytes: int, sink, stream=None) -> None:
     """Plain coalesced read of nbytes at src (the streaming-read reference)."""
-    _check(lib().skgemm_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "skgemm_read_probe")
+    _check(lib().skgemm_read_probe(_ptr(src, nbytes, "src"), nbytes, _ptr(sink, 4 * 512, "sink"),
+                                   _stream(stream)), "skgemm_read_probe")
 
 
 def skgemm_health(stream=None) -> dict:

@@ -87,6 +87,66 @@ def test_argument_checks_before_any_device_work():
     assert lib.skgemm_read_probe(a + 8, 64, a, None) == sk.SKGEMM_EALIGN
 
 
+class _FakeGpuTensor:
+    """Stands in for a GPU tensor on a machine without one. Every call below has
+    an operand that the binding rejects, so the library is never called and the
+    fake address is never used."""
+
+    def __init__(self, nbytes, contiguous=True):
+        self.device = type("D", (), {"type": "cuda"})()
+        self._nbytes, self._contiguous = nbytes, contiguous
+
+    def is_contiguous(self):
+        return self._contiguous
+
+    def numel(self):
+        return self._nbytes // 2
+
+    def element_size(self):
+        return 2
+
+    def data_ptr(self):
+        return 1 << 20
+
+
+def test_binding_rejects_tensors_it_cannot_pass():
+    """The binding refuses host tensors, strided views and buffers shorter than
+    the call reads or writes, with SKGEMM_EINVAL, before anything is launched."""
+    _ensure_built()
+    import torch
+
+    T, N, K = 2, 32, 64
+    host = torch.zeros((N, K), dtype=torch.bfloat16)
+    with pytest.raises(sk.SkgemmError) as e:
+        sk.skgemm_bf16(host, _FakeGpuTensor(2 * T * K), _FakeGpuTensor(2 * T * N), T, N, K, 1)
+    assert e.value.code == sk.SKGEMM_EINVAL and "not on the GPU" in str(e.value)
+    with pytest.raises(sk.SkgemmError) as e:
+        sk.skgemm_bf16(_FakeGpuTensor(2 * N * K, contiguous=False), _FakeGpuTensor(2 * T * K),
+                       _FakeGpuTensor(2 * T * N), T, N, K, 1)
+    assert e.value.code == sk.SKGEMM_EINVAL and "contiguous" in str(e.value)
+    # one byte short, for each operand of each format
+    full = {"W": 2 * N * K, "X": 2 * T * K, "C": 2 * T * N}
+    for short in full:
+        args = {k: _FakeGpuTensor(v - (2 if k == short else 0)) for k, v in full.items()}
+        with pytest.raises(sk.SkgemmError) as e:
+            sk.skgemm_bf16(args["W"], args["X"], args["C"], T, N, K, 1)
+        assert e.value.code == sk.SKGEMM_EINVAL and e.value.args[0].startswith(short + ":")
+    with pytest.raises(sk.SkgemmError) as e:
+        sk.skgemm_mxfp4(_FakeGpuTensor(N * K // 2), _FakeGpuTensor(N * K // 32 - 2), _FakeGpuTensor(2 * T * K),
+                        _FakeGpuTensor(2 * T * N), T, N, 128, 1)
+    assert e.value.args[0].startswith("Wq:")  # K = 128 needs twice the nibbles
+    with pytest.raises(sk.SkgemmError) as e:
+        sk.skgemm_mxfp8(_FakeGpuTensor(N * K), _FakeGpuTensor(N * K // 32 - 2), _FakeGpuTensor(2 * T * K),
+                        _FakeGpuTensor(2 * T * N), T, N, K, 1)
+    assert e.value.args[0].startswith("Wscale:")
+    # batched: the last problem's C ends (L-1)*stride + T*N*2 bytes in
+    L, cs = 3, 2 * T * N + 64
+    with pytest.raises(sk.SkgemmError) as e:
+        sk.skgemm_bf16_batched(_FakeGpuTensor(2 * N * K), _FakeGpuTensor(2 * T * K),
+                               _FakeGpuTensor((L - 1) * cs + 2 * T * N - 2), T, N, K, 1, L, 0, 0, cs)
+    assert e.value.args[0].startswith("C:")
+
+
 def test_strerror_covers_every_code():
     _ensure_built()
     for code in (0, -1, -2, -3, -4, -5):

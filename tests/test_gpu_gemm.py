@@ -122,6 +122,11 @@ def test_bf16_rejects_bad_arguments_without_touching_c():
     with pytest.raises(sk.SkgemmError) as e:
         sk.skgemm_bf16(W.data_ptr() + 2, X, C, 2, 32, 96, 1)
     assert e.value.code == sk.SKGEMM_EALIGN
+    # tensors the binding cannot pass: host memory, a strided view, a short buffer
+    for args in [(W, X.cpu(), C), (W, X, C.t()), (W[:31], X, C), (W, X, C.view(-1)[:63])]:
+        with pytest.raises(sk.SkgemmError) as e:
+            sk.skgemm_bf16(*args, 2, 32, 96, 1)
+        assert e.value.code == sk.SKGEMM_EINVAL
     t.cuda.synchronize()
     assert np.all(bf16_bits(C) == 7)
 
