@@ -36,6 +36,7 @@ BF16_CASES = [
     (9, 48, 192, 2),
     (200, 96, 256, 2),
     (2, 64, 0, 1),
+    (2, 64, 0, 4),
 ]
 
 
@@ -162,7 +163,16 @@ MX_CASES = [
     (40, 2048, 1024, 4),
     (128, 512, 2048, 2),
     (130, 64, 256, 1),
+    (2, 64, 0, 4),  # empty sum: zeros
 ]
+
+
+def assert_zero_or_parity(c, ref, K, what):
+    """K == 0 is an empty sum, stored as +0 everywhere; otherwise parity."""
+    if K == 0:
+        assert np.all(c == 0), f"{what}: an empty sum must store +0"
+        return
+    assert_parity(c, ref, K, what)
 
 
 @pytest.mark.parametrize("T,N,K,S", MX_CASES)
@@ -170,7 +180,7 @@ def test_mxfp4_parity_small(T, N, K, S):
     log(f"mxfp4 parity T={T} N={N} K={K} S={S} tactic={sk.skgemm_tactic_for(T, N, K, S, True)}")
     x, wq, ws = workloads.small_mxfp4_case(T, K, N, seed=3000 + T + N + K + S)
     c = run_mxfp4(x, wq, ws, S)
-    assert_parity(c, G.gemm_mxfp4_ref(x, wq, ws), K, f"mxfp4 T={T} N={N} K={K} S={S}")
+    assert_zero_or_parity(c, G.gemm_mxfp4_ref(x, wq, ws), K, f"mxfp4 T={T} N={N} K={K} S={S}")
 
 
 @pytest.mark.parametrize("S", [1, 4])
@@ -194,6 +204,7 @@ MX8_CASES = [
     (40, 2048, 1024, 4),
     (128, 512, 2048, 2),
     (130, 64, 256, 1),
+    (2, 64, 0, 4),  # empty sum: zeros
 ]
 
 
@@ -201,7 +212,8 @@ MX8_CASES = [
 def test_mxfp8_parity_small(T, N, K, S):
     log(f"mxfp8 parity T={T} N={N} K={K} S={S} tactic={sk.skgemm_tactic_for(T, N, K, S, 2)}")
     x, wq8, ws = workloads.small_mxfp8_case(T, K, N, seed=3500 + T + N + K + S)
-    assert_parity(run_mxfp8(x, wq8, ws, S), G.gemm_mxfp8_ref(x, wq8, ws), K, f"mxfp8 T={T} N={N} K={K} S={S}")
+    assert_zero_or_parity(run_mxfp8(x, wq8, ws, S), G.gemm_mxfp8_ref(x, wq8, ws), K,
+                          f"mxfp8 T={T} N={N} K={K} S={S}")
 
 
 @pytest.mark.parametrize("S", [1, 4])
