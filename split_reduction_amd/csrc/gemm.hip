@@ -923,8 +923,12 @@ void splitk_stream_kernel(GemmParams p) {
       const int tile = tile_at(k);
       const uint32_t old =
           __hip_atomic_fetch_add(cnt_of(tile), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // Last to arrive at a tile its owner gave up on: finish it here.
-      take = owner_of(k) != rank && (old & kAbandon) != 0 && (old & kArrivals) == (uint32_t)(S - 1);
+      // Last to arrive at a tile its owner gave up on: finish it here. That
+      // includes a tile this workgroup owns: the arrival comes from wave
+      // k mod WK, usually not the owner wave, and can land after the owner
+      // wave has given up. Exactly one side finishes: the owner's fetch_or
+      // saw all S arrivals, or the S-th arrival saw the abandon bit.
+      take = (old & kAbandon) != 0 && (old & kArrivals) == (uint32_t)(S - 1);
       if (take) __hip_atomic_store(cnt_of(tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     finish_mask(__builtin_amdgcn_ballot_w64(take), [&](int b) { return k0 + kstep * (j0 + b); }, false);
