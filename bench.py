@@ -1,10 +1,12 @@
 """Benchmark of the split-K decode GEMM on one MI355X.
 
-Prints ONE JSON line. The headline workload is bf16 T=8, K=7168, N=2048,
-split_k=4 (W ~ N(0, 0.02^2), X ~ N(0, 1)); one step is one skgemm_bf16 call
-(the whole hot path: weight stream, X staging, MFMA, LDS and split-K
-reductions, bf16 epilogue). The metric is the weight-stream rate: weight bytes
-per step / step time, in TB/s, and its fraction of the 8 TB/s HBM3E peak.
+Prints ONE JSON line. The headline workload is the largest single-GPU
+configuration: bf16 T=32, K=16384, N=16384, split_k=8 (W ~ N(0, 0.01^2),
+X ~ N(0, 1)), the largest token count of the K = N = 16384 sweep that the
+70 %-of-peak target covers (T <= 32). One step is one skgemm_bf16 call (the
+whole hot path: weight stream, X staging, MFMA, LDS and split-K reductions,
+bf16 epilogue). The metric is the weight-stream rate: weight bytes per step /
+step time, in TB/s, and its fraction of the 8 TB/s HBM3E peak.
 
 Timing protocol:
 * inputs are resident in HBM before the timed region; R copies of the weights
@@ -15,19 +17,23 @@ Timing protocol:
   timed with HIP events recorded on the stream the kernels run on;
 * the same protocol without rotation gives the labelled cache-resident rate.
 
-The other workloads (bf16 T=1 K=1024 N=1024; bf16 T=32 K=7168 N=18432 with
-outlier channels; MXFP4 T=16 K=7168 N=4096; the K = N = 16384 bf16 sweep over
-T) are timed the same way and reported under "workloads". The cpu_baseline
-leg times the fp64 oracle on the host on the headline workload.
+The other workloads (bf16 T=1 K=1024 N=1024; bf16 T=8 K=7168 N=2048; bf16
+T=32 K=7168 N=18432 with outlier channels; MXFP4 and MXFP8 T=16 K=7168
+N=4096; the rest of the K = N = 16384 bf16 sweep over T) are timed the same
+way and reported under "workloads", each with its own roofline block. The
+cpu_baseline leg times the fp64 oracle's GEMM on the host on the headline
+workload (the bf16 -> fp64 conversion of the weights done once, outside the
+timing).
 
 ``--trace-summary DIR`` reads a rocprofv3 kernel trace written under DIR and
 prints per-workload kernel durations (runs of dispatches in time order).
 
-``--pmc-run`` is the short program the HBM counters are taken on: 10 eager
-headline launches on rotated weights, then 5 plain device copies of 256 MiB
-(which read and write exactly 256 MiB each) that calibrate the counters.
-``--pmc-summary DIR`` turns the rocprofv3 counter CSVs under DIR into bytes
-per launch.
+``--pmc-run [WORKLOAD ...|all]`` is the short program the HBM counters are
+taken on: 10 eager launches of each named workload on rotated weights, then 5
+plain device copies of 256 MiB (which read and write exactly 256 MiB each)
+that calibrate the counters. ``--pmc-summary DIR [WORKLOAD ...|all]`` turns
+the rocprofv3 counter CSVs under DIR into bytes per launch for each workload
+and writes ``profiles/traffic_<workload>.json``.
 """
 
 from __future__ import annotations
@@ -52,7 +58,7 @@ import workloads  # noqa: E402
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
 ROTATE_BYTES = 1 << 30
-HEADLINE = "bf16_t8_k7168_n2048"
+HEADLINE = "bf16_sweep_t32_k16384_n16384"
 CSRC = os.path.join("split_reduction_amd", "csrc")
 
 
@@ -236,6 +242,31 @@ class Case:
 BATCH_L = 8  # problems per batched launch reported for the small workloads
 BATCH_MAX_WEIGHT_BYTES = 64 << 20
 
+# Every workload the benchmark reports, the headline first. The K = N = 16384
+# sweep points share one weight matrix (generated once).
+OTHERS = ("bf16_t1_k1024_n1024", "bf16_t8_k7168_n2048", "bf16_t32_k7168_n18432",
+          "mxfp4_t16_k7168_n4096", "mxfp8_t16_k7168_n4096")
+
+
+def all_workloads() -> list:
+    sweep = [workloads.sweep_workload(T).name for T in workloads.SWEEP_T]
+    return [HEADLINE] + list(OTHERS) + [n for n in sweep if n != HEADLINE]
+
+
+def is_sweep(name: str) -> bool:
+    return name.startswith("bf16_sweep_t")
+
+
+def roofline_block(name: str, algo_bytes: int, t_us: float) -> dict:
+    """HBM roofline of one workload's kernel: algorithmic bytes (weights + X +
+    C) per launch over the measured launch time, against the 8 TB/s peak, and
+    the HBM bytes the rocprofv3 counters saw per launch (None unless they were
+    taken on the current kernel sources)."""
+    achieved = algo_bytes / (t_us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": load_traffic(name),
+            "algorithmic_bytes": algo_bytes}
+
 
 def run_workload(wl, steps, warmup, host_w=None) -> dict:
     import split_reduction_amd as sk
@@ -259,6 +290,7 @@ def run_workload(wl, steps, warmup, host_w=None) -> dict:
         "frac_hbm_peak": round(cold["weight_TBps"] * 1000 / HBM_PEAK_GBS, 4),
         "TFLOPs": round(cold["TFLOPs"], 3),
         "frac_mfma_peak": round(cold["TFLOPs"] / BF16_MFMA_PEAK_TFLOPS, 5),
+        "roofline": roofline_block(wl.name, case.algo_bytes(), cold["t_us"]),
         "hot_t_us": round(hot["t_us"], 3),
         "hot_weight_TBps": round(hot["weight_TBps"], 4),
         # The streaming-read reference over the same rotated buffers: what a
@@ -266,8 +298,8 @@ def run_workload(wl, steps, warmup, host_w=None) -> dict:
         "read_probe": {"bytes": probe_bytes, "t_us": round(probe["t_us"], 3),
                        "TBps": round(probe_tbps, 4),
                        "gemm_frac": round(cold["weight_TBps"] / probe_tbps, 4)},
-        "tactic": {k: tac[k] for k in ("nt", "rg", "wk", "wn", "d", "kc", "tile_n", "grid")},
-        "_algo_bytes": case.algo_bytes(),
+        "tactic": {k: tac[k] for k in ("kind", "nt", "wk", "wn", "d", "kc", "tile_n", "grid", "shape",
+                                       "fold", "pdefer")},
     }
     if batched is not None:
         out["batched"] = batched
@@ -283,34 +315,41 @@ def run_workload(wl, steps, warmup, host_w=None) -> dict:
 # ---------------------------------------------------------------------------
 
 
-def cpu_baseline(wl, budget_s: float = 12.0) -> dict:
-    from oracle import gemm
+def cpu_baseline(wl, wb=None, budget_s: float = 12.0) -> dict:
+    """The oracle's fp64 GEMM on the host, timed alone: the weights are
+    decoded to float64 once before the timing (as the oracle's
+    gemm_decoded_ref takes them), then the GEMM is repeated for ``budget_s``."""
+    from oracle import formats, gemm
 
     x = workloads.gen_x(wl)
-    wb = workloads.gen_w_bf16(wl)
+    if wb is None:
+        wb = workloads.gen_w_bf16(wl)
+    w64 = formats.bf16_bits_to_f64(wb)
     try:
         from threadpoolctl import threadpool_info
 
         cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
     except Exception:  # threadpoolctl missing: report the visible CPUs
         cores = os.cpu_count() or 1
-    gemm.gemm_bf16_ref(x, wb)  # first call outside the timing
+    gemm.gemm_decoded_ref(x, w64)  # first call outside the timing
     n = 0
     t0 = time.perf_counter()
     while True:
-        gemm.gemm_bf16_ref(x, wb)
+        gemm.gemm_decoded_ref(x, w64)
         n += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
     per = el / n
+    del w64
     return {
         "value": round(wl.weight_bytes() / per / 1e12, 6),
         "unit": "TB/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"the whole {wl.name} workload (bf16->fp64 conversion and fp64 numpy GEMM), "
-                   f"{n} calls in {el:.1f} s, {per * 1e3:.2f} ms per call"),
+        "sample": (f"the whole {wl.name} workload: the oracle's fp64 numpy GEMM on weights decoded "
+                   f"to fp64 once beforehand, {n} calls in {el:.1f} s, {per * 1e3:.2f} ms per call "
+                   f"({wl.flops() / per / 1e9:.1f} GFLOP/s)"),
     }
 
 
@@ -326,7 +365,7 @@ def trace_summary(path: str, steps: int, warmup: int) -> None:
     and grid. The first run is the headline workload's single launches: per
     timing pass, W eager warmup launches, the graph's untimed first replay and
     its timed replay of K launches; one cold (rotated weights) pass, then one
-    cache-resident pass. Its batched launches follow as a run of their own.
+    cache-resident pass.
     """
     import csv
 
@@ -352,8 +391,6 @@ def trace_summary(path: str, steps: int, warmup: int) -> None:
         d = np.array(durs)
         short = name.replace("void skg::", "").replace("(skg::GemmParams)", "")
         print(f"{i:3d} {len(d):6d} {d.mean():9.3f} {np.median(d):9.3f} {d.min():9.3f} {grid:>8}  {short}")
-    # The headline's single launches: the first run holding both timing
-    # passes (its batched launches, timed afterwards, form a run of their own).
     per_pass = warmup + 2 * steps
     head = [s for s in segs if len(s[1]) >= 2 * per_pass]
     if head:
@@ -366,22 +403,44 @@ def trace_summary(path: str, steps: int, warmup: int) -> None:
             print(f"headline cache-resident timed replay: {len(hot)} launches, avg {hot.mean():.3f} us")
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 counter passes
+# ---------------------------------------------------------------------------
+
 COPY_BYTES = 256 << 20
 PMC_LAUNCHES = 10
 PMC_COPIES = 5
 
 
-def pmc_run(name: str = HEADLINE) -> None:
+def pmc_names(args: list) -> list:
+    if not args or args == ["all"]:
+        return all_workloads() if args == ["all"] else [HEADLINE]
+    return list(args)
+
+
+def pmc_run(names: list) -> None:
+    """PMC_LAUNCHES eager launches of each workload in turn (rotated weights),
+    then the calibration copies. Progress goes to stderr per workload."""
     import torch
 
     import split_reduction_amd as sk
 
-    head = workloads.get(name)
-    case = Case(head)
+    sweep_w = None
     stream = torch.cuda.current_stream()
-    for i in range(PMC_LAUNCHES):
-        case.launch(i, stream)
-    torch.cuda.synchronize()
+    for name in names:
+        wl = workloads.get(name)
+        host_w = None
+        if is_sweep(name):
+            if sweep_w is None:
+                sweep_w = workloads.gen_w_bf16(workloads.sweep_workload(1))
+            host_w = sweep_w
+        case = Case(wl, host_w)
+        for i in range(PMC_LAUNCHES):
+            case.launch(i, stream)
+        torch.cuda.synchronize()
+        del case
+        torch.cuda.empty_cache()
+        log(f"pmc-run {name}: {PMC_LAUNCHES} launches")
     src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0").random_()
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -389,122 +448,154 @@ def pmc_run(name: str = HEADLINE) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     del sk
-    print(json.dumps({"pmc_run": name, "launches": PMC_LAUNCHES, "copies": PMC_COPIES,
+    print(json.dumps({"pmc_run": names, "launches": PMC_LAUNCHES, "copies": PMC_COPIES,
                       "copy_bytes": COPY_BYTES}))
 
 
-def pmc_summary(path: str, name: str = HEADLINE) -> dict:
-    """HBM bytes per headline launch from the FETCH_SIZE and WRITE_SIZE passes
-    of ``--pmc-run`` under ``path`` (KiB per dispatch, each scaled by what the
-    same counter reads for the 256 MiB calibration copies: the last
-    ``copies`` copyBuffer dispatches of the run)."""
-    import csv
-
-    per = {}
-    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-        rows = []
-        for f in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
-            with open(f) as fh:
-                rows += [r for r in csv.DictReader(fh) if r.get("Counter_Name") == counter]
-        if not rows:
-            raise SystemExit(f"no {counter} rows under {path}")
-        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-        gemm = [float(r["Counter_Value"]) for r in rows if "splitk_" in r["Kernel_Name"]]
-        kernels = sorted({r["Kernel_Name"] for r in rows if "splitk_" in r["Kernel_Name"]})
-        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-PMC_COPIES:]
-        if len(gemm) != PMC_LAUNCHES or len(copies) != PMC_COPIES or len(kernels) != 1:
-            raise SystemExit(f"{counter}: {len(gemm)} GEMM dispatches of {kernels}, {len(copies)} copies")
-        per[counter] = (float(np.mean(gemm)), float(np.mean(copies)), kernels[0])
-    fetch, fetch_copy, kname = per["FETCH_SIZE"]
-    write, write_copy, _ = per["WRITE_SIZE"]
-    fetch_factor = fetch_copy * 1024 / COPY_BYTES
-    write_factor = write_copy * 1024 / COPY_BYTES
-    rd = fetch * 1024 / fetch_factor
-    wr = write * 1024 / write_factor
-    head = workloads.get(name)
-    algo = head.weight_bytes() + head.T * head.K * 2 + head.T * head.N * 2
-    out = {
-        "workload": name,
-        "kernel": kname.split("(")[0].replace("void ", ""),
-        "kernel_source_sha": kernel_source_hash(),
-        "fetch_size_kib_per_launch": round(fetch, 1),
-        "write_size_kib_per_launch": round(write, 1),
-        "copy_calibration": {
-            "bytes_read_and_written": COPY_BYTES,
-            "fetch_size_kib": round(fetch_copy, 1),
-            "write_size_kib": round(write_copy, 1),
-            "fetch_kib_x1024_per_byte": round(fetch_factor, 4),
-            "write_kib_x1024_per_byte": round(write_factor, 4),
-        },
-        "hbm_read_bytes_per_launch": int(round(rd)),
-        "hbm_write_bytes_per_launch": int(round(wr)),
-        "hbm_bytes_per_launch": int(round(rd + wr)),
-        "algorithmic_bytes_per_launch": algo,
-        "commands": [
-            "cd /tmp && timeout -s KILL 150 rocprofv3 --pmc FETCH_SIZE --output-format csv "
-            f"-d $R/gpurun_out/pmc/fetch -o fetch -- python3 $R/bench.py --pmc-run {name}",
-            "cd /tmp && timeout -s KILL 150 rocprofv3 --pmc WRITE_SIZE --output-format csv "
-            f"-d $R/gpurun_out/pmc/write -o write -- python3 $R/bench.py --pmc-run {name}",
-            f"python bench.py --pmc-summary gpurun_out/pmc {name}",
-        ],
-        "note": (f"R is the repository root. Counters are per dispatch: {PMC_LAUNCHES} headline "
-                 f"launches on rotated weights, then {PMC_COPIES} copies of {COPY_BYTES >> 20} MiB "
-                 "whose counter readings calibrate KiB per byte moved."),
-    }
-    print(json.dumps(out, indent=1))
-    return out
-
-
-def mfma_summary(path: str, name: str = HEADLINE) -> dict:
-    """Matrix-core use of a workload's kernel from one ``--pmc MfmaUtil
-    MfmaFlopsBF16`` pass of ``--pmc-run`` under ``path`` (rocprofv3's derived
-    counters: MFMA busy cycles over all SIMDs / (GPU active cycles x SIMDs),
-    and BF16 MFMA operations x 512), per dispatch, averaged over the
-    workload's launches."""
+def _counter_rows(path: str, counter: str) -> list:
     import csv
 
     rows = []
     for f in sorted(glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)):
         with open(f) as fh:
-            rows += [r for r in csv.DictReader(fh) if "splitk_" in r.get("Kernel_Name", "")]
+            rows += [r for r in csv.DictReader(fh) if r.get("Counter_Name") == counter]
     if not rows:
-        raise SystemExit(f"no GEMM counter rows under {path}")
-    val = {}
-    kernels = sorted({r["Kernel_Name"] for r in rows})
-    for counter in ("MfmaUtil", "MfmaFlopsBF16"):
-        v = [float(r["Counter_Value"]) for r in rows if r.get("Counter_Name") == counter]
-        if len(v) != PMC_LAUNCHES or len(kernels) != 1:
-            raise SystemExit(f"{counter}: {len(v)} GEMM dispatches of {kernels}")
-        val[counter] = float(np.mean(v))
-    wl = workloads.get(name)
-    flops = wl.flops()
-    out = {
-        "workload": name,
-        "kernel": kernels[0].split("(")[0].replace("void ", ""),
-        "kernel_source_sha": kernel_source_hash(),
-        "mfma_util_percent": round(val["MfmaUtil"], 2),
-        "mfma_flops_bf16_per_launch": int(round(val["MfmaFlopsBF16"])),
-        "algorithmic_flops_per_launch": flops,
-        "executed_over_algorithmic": round(val["MfmaFlopsBF16"] / flops, 3),
-        "commands": [
-            "cd /tmp && timeout -s KILL 150 rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv "
-            f"-d $R/gpurun_out/mfma_{name} -o mfma -- python3 $R/bench.py --pmc-run {name}",
-            f"python bench.py --mfma-summary gpurun_out/mfma_{name} {name}",
-        ],
-        "note": ("R is the repository root. Executed MFMA flops exceed 2*T*N*K by the token padding to "
-                 "16 and, in folded tiles, by the off-diagonal blocks that are computed and not read."),
-    }
-    print(json.dumps(out, indent=1))
+        raise SystemExit(f"no {counter} rows under {path}")
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def _per_workload(rows: list, names: list) -> list:
+    """The GEMM dispatches of a --pmc-run, cut into consecutive groups of
+    PMC_LAUNCHES, one per workload in run order: [(kernel, [values])]."""
+    gemm = [r for r in rows if "splitk_" in r["Kernel_Name"]]
+    if len(gemm) != PMC_LAUNCHES * len(names):
+        raise SystemExit(f"{len(gemm)} GEMM dispatches for {len(names)} workloads")
+    out = []
+    for i, _ in enumerate(names):
+        grp = gemm[i * PMC_LAUNCHES:(i + 1) * PMC_LAUNCHES]
+        kernels = {r["Kernel_Name"] for r in grp}
+        if len(kernels) != 1:
+            raise SystemExit(f"workload {names[i]}: kernels {kernels}")
+        out.append((kernels.pop(), [float(r["Counter_Value"]) for r in grp]))
     return out
+
+
+def pmc_summary(path: str, names: list) -> list:
+    """HBM bytes per launch of each workload from the FETCH_SIZE and
+    WRITE_SIZE passes of ``--pmc-run`` under ``path`` (KiB per dispatch, each
+    scaled by what the same counter reads for the 256 MiB calibration copies:
+    the last PMC_COPIES copyBuffer dispatches of the run). Writes
+    profiles/traffic_<workload>.json per workload and profiles/traffic_summary.md."""
+    per = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        rows = _counter_rows(os.path.join(path, counter.split("_")[0].lower()), counter)
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]][-PMC_COPIES:]
+        if len(copies) != PMC_COPIES:
+            raise SystemExit(f"{counter}: {len(copies)} calibration copies")
+        per[counter] = (_per_workload(rows, names), float(np.mean(copies)))
+    fetch_factor = per["FETCH_SIZE"][1] * 1024 / COPY_BYTES
+    write_factor = per["WRITE_SIZE"][1] * 1024 / COPY_BYTES
+    sha = kernel_source_hash()
+    outs = []
+    table = ["| workload | kernel | HBM read / launch | HBM write / launch | total | algorithmic (W+X+C) | ratio |",
+             "|---|---|---|---|---|---|---|"]
+    for i, name in enumerate(names):
+        kname, fetch = per["FETCH_SIZE"][0][i]
+        _, write = per["WRITE_SIZE"][0][i]
+        fetch, write = float(np.mean(fetch)), float(np.mean(write))
+        rd = fetch * 1024 / fetch_factor
+        wr = write * 1024 / write_factor
+        wl = workloads.get(name)
+        algo = wl.weight_bytes() + wl.T * wl.K * 2 + wl.T * wl.N * 2
+        kshort = kname.split("(")[0].replace("void ", "")
+        out = {
+            "workload": name,
+            "kernel": kshort,
+            "kernel_source_sha": sha,
+            "fetch_size_kib_per_launch": round(fetch, 1),
+            "write_size_kib_per_launch": round(write, 1),
+            "copy_calibration": {
+                "bytes_read_and_written": COPY_BYTES,
+                "fetch_size_kib": round(per["FETCH_SIZE"][1], 1),
+                "write_size_kib": round(per["WRITE_SIZE"][1], 1),
+                "fetch_kib_x1024_per_byte": round(fetch_factor, 4),
+                "write_kib_x1024_per_byte": round(write_factor, 4),
+            },
+            "hbm_read_bytes_per_launch": int(round(rd)),
+            "hbm_write_bytes_per_launch": int(round(wr)),
+            "hbm_bytes_per_launch": int(round(rd + wr)),
+            "algorithmic_bytes_per_launch": algo,
+            "commands": [
+                "cd /tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv "
+                "-d $R/gpurun_out/pmc/fetch -o fetch -- python3 $R/bench.py --pmc-run all",
+                "cd /tmp && timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv "
+                "-d $R/gpurun_out/pmc/write -o write -- python3 $R/bench.py --pmc-run all",
+                "python bench.py --pmc-summary gpurun_out/pmc all",
+            ],
+            "note": (f"R is the repository root. Counters are per dispatch: {PMC_LAUNCHES} launches of each "
+                     f"workload on rotated weights, then {PMC_COPIES} copies of {COPY_BYTES >> 20} MiB whose "
+                     "counter readings calibrate KiB per byte moved."),
+        }
+        with open(os.path.join(ROOT, "profiles", f"traffic_{name}.json"), "w") as f:
+            json.dump(out, f, indent=1)
+            f.write("\n")
+        outs.append(out)
+        table.append(f"| {name} | `{kshort}` | {rd / 1e6:.2f} MB | {wr / 1e6:.3f} MB | {(rd + wr) / 1e6:.2f} MB "
+                     f"| {algo / 1e6:.2f} MB | {(rd + wr) / algo:.3f} |")
+    with open(os.path.join(ROOT, "profiles", "traffic_summary.md"), "w") as f:
+        f.write("# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)\n\n")
+        f.write(f"Kernel sources: `{sha}`. Counters calibrated on {PMC_COPIES} plain device copies of "
+                f"{COPY_BYTES >> 20} MiB: FETCH_SIZE reads {fetch_factor:.4f} KiB x 1024 per byte read, "
+                f"WRITE_SIZE {write_factor:.4f} per byte written.\n\n")
+        f.write("Commands (R = repository root):\n\n")
+        for c in outs[0]["commands"]:
+            f.write(f"    {c}\n")
+        f.write("\n" + "\n".join(table) + "\n")
+    print("\n".join(table))
+    return outs
+
+
+def mfma_summary(path: str, names: list) -> list:
+    """Matrix-core use of each workload's kernel from one ``--pmc MfmaUtil
+    MfmaFlopsBF16`` pass of ``--pmc-run`` under ``path`` (rocprofv3's derived
+    counters: MFMA busy cycles over all SIMDs / (GPU active cycles x SIMDs),
+    and BF16 MFMA operations x 512), per dispatch, averaged over the
+    workload's launches. Writes profiles/mfma_summary.md."""
+    sha = kernel_source_hash()
+    util = _per_workload(_counter_rows(path, "MfmaUtil"), names)
+    flops = _per_workload(_counter_rows(path, "MfmaFlopsBF16"), names)
+    table = ["| workload | kernel | MfmaUtil % | MFMA bf16 flops / launch | 2TNK | executed / algorithmic |",
+             "|---|---|---|---|---|---|"]
+    outs = []
+    for i, name in enumerate(names):
+        wl = workloads.get(name)
+        kname = util[i][0].split("(")[0].replace("void ", "")
+        u = float(np.mean(util[i][1]))
+        fl = float(np.mean(flops[i][1]))
+        outs.append({"workload": name, "kernel": kname, "mfma_util_percent": round(u, 2),
+                     "mfma_flops_bf16_per_launch": int(round(fl)), "algorithmic_flops_per_launch": wl.flops()})
+        table.append(f"| {name} | `{kname}` | {u:.2f} | {fl:.4g} | {wl.flops():.4g} | {fl / wl.flops():.3f} |")
+    with open(os.path.join(ROOT, "profiles", "mfma_summary.md"), "w") as f:
+        f.write("# Matrix-core use per launch (rocprofv3 MfmaUtil, MfmaFlopsBF16)\n\n")
+        f.write(f"Kernel sources: `{sha}`. Command (R = repository root):\n\n"
+                "    cd /tmp && timeout -s KILL 300 rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv "
+                "-d $R/gpurun_out/mfma -o mfma -- python3 $R/bench.py --pmc-run all\n"
+                "    python bench.py --mfma-summary gpurun_out/mfma all\n\n"
+                "Executed MFMA flops exceed 2*T*N*K by the token padding to 16 and, in folded tiles, by "
+                "the off-diagonal blocks that are computed and not read.\n\n")
+        f.write("\n".join(table) + "\n")
+    print("\n".join(table))
+    return outs
 
 
 # ---------------------------------------------------------------------------
 
 
-def load_traffic(headline_name: str):
-    """HBM bytes per launch measured by rocprofv3 counters, if they were taken
-    on the current kernel source (else None)."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{headline_name}.json")
+def load_traffic(name: str):
+    """HBM bytes per launch measured by rocprofv3 counters for a workload, if
+    they were taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -522,21 +613,21 @@ def main() -> None:
     ap.add_argument("--only-headline", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--trace-summary", metavar="DIR", help="summarise a rocprofv3 kernel trace and exit")
-    ap.add_argument("--pmc-run", nargs="?", const=HEADLINE, metavar="WORKLOAD",
-                    help="the short run HBM counters are taken on (default: the headline)")
+    ap.add_argument("--pmc-run", nargs="*", metavar="WORKLOAD",
+                    help="the short run counters are taken on (default: the headline; 'all': every workload)")
     ap.add_argument("--mfma-summary", nargs="+", metavar=("DIR", "WORKLOAD"),
                     help="summarise an MfmaUtil / MfmaFlopsBF16 counter pass of --pmc-run and exit")
     ap.add_argument("--pmc-summary", nargs="+", metavar=("DIR", "WORKLOAD"),
-                    help="summarise rocprofv3 counter CSVs under DIR (for WORKLOAD) and exit")
+                    help="summarise the FETCH_SIZE / WRITE_SIZE passes under DIR and exit")
     args = ap.parse_args()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary[:2])
+        pmc_summary(args.pmc_summary[0], pmc_names(args.pmc_summary[1:]))
         return
     if args.mfma_summary:
-        mfma_summary(*args.mfma_summary[:2])
+        mfma_summary(args.mfma_summary[0], pmc_names(args.mfma_summary[1:]))
         return
-    if args.pmc_run:
-        pmc_run(args.pmc_run)
+    if args.pmc_run is not None:
+        pmc_run(pmc_names(args.pmc_run))
         return
     if args.trace_summary:
         trace_summary(args.trace_summary, args.steps, args.warmup)
@@ -557,37 +648,29 @@ def main() -> None:
     sk.lib()
     torch.cuda.init()
 
-    head = workloads.WORKLOADS[HEADLINE]
+    head = workloads.get(HEADLINE)
+    log("sweep weights K = N = 16384")
+    wsweep = workloads.gen_w_bf16(workloads.sweep_workload(1))
     log(f"headline {head.name}")
-    h = run_workload(head, args.steps, args.warmup)
-    log(json.dumps({k: v for k, v in h.items() if not k.startswith("_")}))
+    h = run_workload(head, args.steps, args.warmup, host_w=wsweep)
+    log(json.dumps(h))
 
     extra = []
     if not args.only_headline:
         steps = max(20, args.steps // 2)
         warm = max(3, args.warmup // 2)
-        for name in ("bf16_t1_k1024_n1024", "bf16_t32_k7168_n18432", "mxfp4_t16_k7168_n4096",
-                     "mxfp8_t16_k7168_n4096"):
+        for name in all_workloads()[1:]:
             log(f"workload {name}")
-            r = run_workload(workloads.WORKLOADS[name], steps, warm)
-            log(json.dumps({k: v for k, v in r.items() if not k.startswith("_")}))
+            r = run_workload(workloads.get(name), steps, warm, host_w=wsweep if is_sweep(name) else None)
+            log(json.dumps(r))
             extra.append(r)
-        log("sweep weights K = N = 16384")
-        sw = workloads.sweep_workload(1)
-        wsweep = workloads.gen_w_bf16(sw)
-        for T in workloads.SWEEP_T:
-            r = run_workload(workloads.sweep_workload(T), steps, warm, host_w=wsweep)
-            log(json.dumps({k: v for k, v in r.items() if not k.startswith("_")}))
-            extra.append(r)
-        del wsweep
 
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(head)
+        cpu = cpu_baseline(head, wsweep)
+    del wsweep
 
-    t_s = h["t_us"] * 1e-6
-    achieved = h["_algo_bytes"] / t_s / 1e9
     line = {
         "metric": "weight-stream HBM TB/s (% of peak) + TFLOP/s, split-K decode GEMM, 1 GPU",
         "value": h["weight_TBps"],
@@ -605,25 +688,17 @@ def main() -> None:
         "TFLOPs": h["TFLOPs"],
         "config": {
             "workload": head.name, "T": head.T, "K": head.K, "N": head.N,
-            "split_k": head.split_k, "weights": "bf16 N(0,0.02^2)", "activations": "bf16 N(0,1)",
+            "split_k": head.split_k, "weights": "bf16 N(0,0.01^2)", "activations": "bf16 N(0,1)",
             "cache": f"cold: {h['rotated_copies']} rotated weight copies (>= 1 GiB)",
             "timing": "HIP graph of exactly `steps` launches, HIP events on the launch stream",
             "parallelism": "single GPU",
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": load_traffic(head.name),
-        },
+        "roofline": h["roofline"],
         "cpu_baseline": cpu,
         "hot_cache": {"t_us": h["hot_t_us"], "weight_TBps": h["hot_weight_TBps"]},
         "read_probe": h["read_probe"],
-        "batched": h.get("batched"),
         "tactic": h["tactic"],
-        "workloads": [{k: v for k, v in r.items() if not k.startswith("_")} for r in extra],
+        "workloads": extra,
         "kernel_source_sha": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -148,7 +148,12 @@ SKGEMM_API int skgemm_mxfp8_batched(const void* Wq8, const void* Wscale, const v
  * workspace is FP32 partials [split_k, min(T,128), N] and one uint32 counter
  * per 16 output rows, each on a 128-byte line of its own; counters return to
  * zero at the end of every call.
- * May synchronise `stream` when it replaces a smaller workspace.
+ * Workspace lifetime: a workspace that has to grow is replaced by a new,
+ * larger one; the old one is not freed but kept until skgemm_release, because
+ * a graph captured while it was current still uses it on every replay. So a
+ * graph may be captured after skgemm_reserve and replayed after later eager
+ * calls of any size on the same stream. skgemm_release frees every
+ * workspace: graphs that use one must not be replayed after it.
  */
 SKGEMM_API int skgemm_reserve(int max_T, int max_N, int max_split_k, hipStream_t stream);
 
@@ -262,6 +267,33 @@ SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int weight_fo
  * buf = NULL to turn stamping off (the default). Process-wide setting.
  */
 SKGEMM_API int skgemm_set_timeline(void* buf, size_t capacity);
+
+/*
+ * skgemm_set_override: pins a choice the library normally makes itself; for
+ * tests and tuning runs, not needed in normal use (nothing else, no
+ * environment variable, changes which kernel a call runs). value -1 restores
+ * the library's own choice; other negative values and unknown knobs give
+ * SKGEMM_EINVAL. Process-wide, read by every later call and by
+ * skgemm_tactic_for; a pinned kernel kind or shape that cannot take a call's
+ * sizes makes that call return SKGEMM_ESHAPE instead of choosing another.
+ * Every value keeps results within the stated bounds (the hand-off choices
+ * change no bits at all).
+ */
+enum skgemm_knob {
+  SKGEMM_KNOB_KIND = 0,        /* 0 one tile per workgroup, 1 persistent, 2 all
+                                  ranks in one workgroup, 3 wide tiles        */
+  SKGEMM_KNOB_STREAM = 1,      /* persistent kernel: shape index 0..6         */
+  SKGEMM_KNOB_SHAPE = 2,       /* one-tile-per-workgroup kernel: shape 0..7   */
+  SKGEMM_KNOB_FOLD = 3,        /* all-ranks kernel: largest K fold 1, 2, 4, 8 */
+  SKGEMM_KNOB_CLUSTER_C = 4,   /* all-ranks kernel: bf16 pieces per lane 1, 2 */
+  SKGEMM_KNOB_WG_PER_CU = 5,   /* persistent kernel: workgroups per CU        */
+  SKGEMM_KNOB_PDEFER = 6,      /* persistent kernel: partials held in LDS 0/1 */
+  SKGEMM_KNOB_OWNER_WAIT = 7,  /* owner wait bound, 100 MHz ticks (0: hand the
+                                  tile over at once)                          */
+  SKGEMM_KNOB_HANDOFF = 8      /* persistent kernel's split-K hand-off:
+                                  0 arrival counter, 1 tagged mailbox         */
+};
+SKGEMM_API int skgemm_set_override(int knob, int value);
 
 /* skgemm_strerror: static text for a return code. */
 SKGEMM_API const char* skgemm_strerror(int code);

@@ -32,36 +32,29 @@ import numpy as np
 from .formats import bf16_bits_to_f64, mxfp4_dequant_f64, mxfp8_dequant_f64
 
 
-def gemm_bf16_ref(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
-    """C[T, N] float64 = X[T, K] . W[N, K]^T from bf16 bit patterns (uint16)."""
+def gemm_decoded_ref(x_bits: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """C[T, N] float64 = X[T, K] . W[N, K]^T with X as bf16 bit patterns and W
+    already holding exact float64 weight values (a decoded weight matrix, kept
+    by a caller that multiplies several X by one large W)."""
     x = bf16_bits_to_f64(x_bits)
-    w = bf16_bits_to_f64(w_bits)
     if x.ndim != 2 or w.ndim != 2 or x.shape[1] != w.shape[1]:
         raise ValueError(f"shape mismatch X{x.shape} W{w.shape}")
     return x @ w.T
 
 
-def gemm_rows_ref(x_bits: np.ndarray, w_bits_rows: np.ndarray) -> np.ndarray:
-    """Same product for a sample of weight rows: C[:, rows] of the full GEMM."""
-    return gemm_bf16_ref(x_bits, w_bits_rows)
+def gemm_bf16_ref(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """C[T, N] float64 = X[T, K] . W[N, K]^T from bf16 bit patterns (uint16)."""
+    return gemm_decoded_ref(x_bits, bf16_bits_to_f64(w_bits))
 
 
 def gemm_mxfp4_ref(x_bits: np.ndarray, wq: np.ndarray, wscale: np.ndarray) -> np.ndarray:
     """C[T, N] float64 = X . dequant(Wq, Wscale)^T."""
-    x = bf16_bits_to_f64(x_bits)
-    w = mxfp4_dequant_f64(wq, wscale)
-    if x.shape[1] != w.shape[1]:
-        raise ValueError(f"shape mismatch X{x.shape} W{w.shape}")
-    return x @ w.T
+    return gemm_decoded_ref(x_bits, mxfp4_dequant_f64(wq, wscale))
 
 
 def gemm_mxfp8_ref(x_bits: np.ndarray, wq8: np.ndarray, wscale: np.ndarray) -> np.ndarray:
     """C[T, N] float64 = X . dequant(Wq8, Wscale)^T (E4M3 elements, E8M0 block scales)."""
-    x = bf16_bits_to_f64(x_bits)
-    w = mxfp8_dequant_f64(wq8, wscale)
-    if x.shape[1] != w.shape[1]:
-        raise ValueError(f"shape mismatch X{x.shape} W{w.shape}")
-    return x @ w.T
+    return gemm_decoded_ref(x_bits, mxfp8_dequant_f64(wq8, wscale))
 
 
 def gemm_bruteforce(x_vals, w_vals) -> list:

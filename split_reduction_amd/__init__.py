@@ -26,6 +26,10 @@ SKGEMM_ESHAPE = -3
 SKGEMM_ENOMEM = -4
 SKGEMM_EHIP = -5
 
+# skgemm_set_override knobs (include/skgemm.h, enum skgemm_knob)
+KNOBS = {"kind": 0, "stream": 1, "shape": 2, "fold": 3, "cluster_c": 4, "wg_per_cu": 5,
+         "pdefer": 6, "owner_wait": 7, "handoff": 8}
+
 _lib = None
 
 
@@ -57,6 +61,7 @@ def _declare(lib):
         "skgemm_set_timeline": [vp, sz],
         "skgemm_read_probe": [vp, sz, vp, st],
         "skgemm_health": [vp, sz, st],
+        "skgemm_set_override": [i, i],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -285,3 +290,16 @@ def skgemm_strerror(code: int) -> str:
 
 def skgemm_last_hip_error() -> int:
     return lib().skgemm_last_hip_error()
+
+
+def skgemm_set_override(knob, value: int) -> None:
+    """Pin a choice the library otherwise makes itself (tests and tuning runs);
+    knob is a name of ``KNOBS`` or its number, value -1 restores the default."""
+    k = KNOBS[knob] if isinstance(knob, str) else int(knob)
+    _check(lib().skgemm_set_override(k, int(value)), "skgemm_set_override")
+
+
+def clear_overrides() -> None:
+    """Restore the library's own choice for every knob."""
+    for k in KNOBS.values():
+        _check(lib().skgemm_set_override(k, -1), "skgemm_set_override")

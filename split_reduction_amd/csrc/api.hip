@@ -10,6 +10,7 @@
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "skgemm.h"
 #include "skgemm_internal.h"
@@ -21,16 +22,16 @@ constexpr int kTokenBlock = 128;  // rows of X / C per launch (16 * 8 MFMA tiles
 
 thread_local int g_last_hip_error = 0;
 
-// Optional phase-stamp buffer (skgemm_set_timeline).
-// How long a tile's owner waits for the other split ranks before handing the
-// tile to the last to arrive: 100 us of the 100 MHz device clock, unless
-// SKGEMM_OWNER_WAIT gives another tick count (tests set 0 to exercise the
-// hand-over path).
-uint32_t owner_wait_ticks() {
-  const char* e = getenv("SKGEMM_OWNER_WAIT");
-  return e ? (uint32_t)strtoul(e, nullptr, 10) : 10000u;
-}
+// Pinned choices (skgemm_set_override), stored as value + 1: 0 (the initial
+// state) means the library's own choice.
+std::atomic<int> g_knobs[skg::kKnobCount];
 
+// How long a tile's owner waits for the other split ranks before handing the
+// tile to the last to arrive: 100 us of the 100 MHz device clock unless a
+// test pins another tick count (0 exercises the hand-over path).
+uint32_t owner_wait_ticks() { return (uint32_t)skg::knob(skg::kKnobOwnerWait, 10000); }
+
+// Optional phase-stamp buffer (skgemm_set_timeline).
 std::atomic<uint64_t*> g_stamps{nullptr};
 std::atomic<size_t> g_stamps_cap{0};
 
@@ -76,10 +77,15 @@ struct Workspace {
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Workspaces replaced by larger ones, kept until skgemm_release: a HIP graph
+// captured earlier still names their addresses in its kernel arguments, so
+// freeing them would let a later replay write into memory handed out again.
+std::vector<std::pair<int, Workspace>> g_retired;
 
 // Makes the stream's workspace hold at least part_bytes of partials and
-// cnt_count zeroed counters. Growing frees the old buffers after the stream
-// drains; under graph capture it refuses instead.
+// cnt_count zeroed counters. Growing allocates new buffers and retires the old
+// ones (kept allocated until skgemm_release); under graph capture it refuses
+// instead.
 int ensure_workspace(hipStream_t stream, size_t part_bytes, size_t cnt_count, Workspace* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -94,13 +100,6 @@ int ensure_workspace(hipStream_t stream, size_t part_bytes, size_t cnt_count, Wo
   e = hipStreamIsCapturing(stream, &st);
   if (e != hipSuccess) return hip_fail(e);
   if (st != hipStreamCaptureStatusNone) return SKGEMM_ENOMEM;
-  if (w.part != nullptr || w.cnt != nullptr) {
-    e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_fail(e);
-    if (w.part) (void)hipFree(w.part);
-    if (w.cnt) (void)hipFree(w.cnt);
-    w = Workspace{};
-  }
   Workspace nw;
   nw.part_bytes = std::max(part_bytes, (size_t)256);
   nw.cnt_count = std::max(cnt_count, (size_t)64);
@@ -116,6 +115,7 @@ int ensure_workspace(hipStream_t stream, size_t part_bytes, size_t cnt_count, Wo
     (void)hipFree(nw.cnt);
     return hip_fail(e);
   }
+  if (w.part != nullptr || w.cnt != nullptr) g_retired.emplace_back(dev, w);
   w = nw;
   *out = w;
   return SKGEMM_OK;
@@ -213,6 +213,12 @@ int run_gemm(int wf, const void* w, const void* ws, const void* x, void* c, int 
 
 }  // namespace
 
+int skg::knob(int k, int dflt) {
+  if (k < 0 || k >= skg::kKnobCount) return dflt;
+  const int v = g_knobs[k].load(std::memory_order_relaxed);
+  return v == 0 ? dflt : v - 1;
+}
+
 extern "C" {
 
 SKGEMM_API int skgemm_bf16(const void* W, const void* X, void* C, int T, int N, int K,
@@ -288,14 +294,17 @@ SKGEMM_API int skgemm_release(void) {
   // current device is restored afterwards.
   int caller_dev = -1;
   if (hipGetDevice(&caller_dev) != hipSuccess) caller_dev = -1;
-  for (auto& kv : g_ws) {
-    hipError_t e = hipSetDevice(kv.first.first);
+  std::vector<std::pair<int, Workspace>> all(g_retired.begin(), g_retired.end());
+  for (auto& kv : g_ws) all.emplace_back(kv.first.first, kv.second);
+  for (auto& dw : all) {
+    hipError_t e = hipSetDevice(dw.first);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) rc = hip_fail(e);
-    if (kv.second.part) (void)hipFree(kv.second.part);
-    if (kv.second.cnt) (void)hipFree(kv.second.cnt);
+    if (dw.second.part) (void)hipFree(dw.second.part);
+    if (dw.second.cnt) (void)hipFree(dw.second.cnt);
   }
   g_ws.clear();
+  g_retired.clear();
   if (caller_dev >= 0) {
     const hipError_t e = hipSetDevice(caller_dev);
     if (e != hipSuccess && rc == SKGEMM_OK) rc = hip_fail(e);
@@ -410,6 +419,12 @@ SKGEMM_API int skgemm_read_probe(const void* src, size_t bytes, uint32_t* sink, 
     return SKGEMM_EALIGN;
   const hipError_t e = skg::launch_read_probe(src, bytes, sink, stream);
   return e == hipSuccess ? SKGEMM_OK : hip_fail(e);
+}
+
+SKGEMM_API int skgemm_set_override(int knob, int value) {
+  if (knob < 0 || knob >= skg::kKnobCount || value < -1) return SKGEMM_EINVAL;
+  g_knobs[knob].store(value + 1, std::memory_order_relaxed);
+  return SKGEMM_OK;
 }
 
 SKGEMM_API const char* skgemm_strerror(int code) {

@@ -24,7 +24,10 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Word 3 of a gfx9 raw buffer descriptor: 32-bit data format, no swizzle.
 constexpr int kRsrcWord3 = 0x00020000;
-// An offset past every bound this library builds (bounds stay below 2^31).
+// An offset at or past every bound this library builds. The host keeps each
+// resource's span at most 2^31 bytes: per-tile resources by the size limits
+// (at most 256 rows of at most 2^23 bytes), whole-matrix resources by an
+// explicit check where the kernel that uses them is chosen.
 constexpr uint32_t kOOB = 0x80000000u;
 // Cache-policy bits of a buffer access on gfx950: bit 1 is NT (streaming).
 constexpr int kPolicyDefault = 0;
@@ -109,8 +112,23 @@ __device__ __forceinline__ void line_pair_to_operands(u32x4 l0, u32x4 l1, u32x4&
   }
 }
 
+// Compiler-only ordering point of the split-K hand-offs. Their counters are
+// relaxed device-scope atomics and their partials device-coherent buffer
+// accesses; the hardware order between the two comes from s_waitcnt (stores
+// complete before the arrival is issued) and from data dependence (partials
+// are loaded only after a branch on the counter's value). A relaxed atomic
+// does not stop the compiler from moving other memory accesses across it, so
+// each side of the hand-off puts this fence between the two.
+__device__ __forceinline__ void handoff_order() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
 // Waits until every vector memory access this wave issued has completed
-// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima).
-__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left at their maxima). The wait
+// intrinsic itself is not a memory operation to the compiler, so fences on
+// both sides keep every access on its side of the wait.
+__device__ __forceinline__ void wait_vmem_all() {
+  handoff_order();
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  handoff_order();
+}
 
 }  // namespace skg

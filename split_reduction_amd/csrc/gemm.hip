@@ -38,8 +38,6 @@
 //    and e8m0_f32). The activations are staged with the same K permutation,
 //    which leaves the contraction unchanged.
 
-#include <stdlib.h>
-
 #include "device/mfma.h"
 #include "device/pack.h"
 #include "device/types.h"
@@ -112,7 +110,8 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
   const int n0 = tile * TILE_N;
   const int kbase = rank * p.ks;
 
-  // Weight rows of this tile (byte bounds below 2^31, checked on the host).
+  // Weight rows of this tile: the resource starts at the tile's first row, so
+  // its span is TILE_N rows (at most 256 rows of at most 2^23 bytes: 2^31).
   const uint32_t wrow_bytes = row_bytes(WF, (uint32_t)K);
   const rsrc_t wr = make_rsrc(static_cast<const uint8_t*>(p.w) + (size_t)n0 * wrow_bytes,
                               TILE_N * wrow_bytes);
@@ -323,6 +322,7 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
   }
   __syncthreads();
   if (s_last == 0 || !owner) return;
+  handoff_order();  // the partial loads below stay after the arrival
 
   // The last rank to arrive sums the ranks' partials in rank order 0..S-1,
   // taking its own from registers, rounds once and stores C once.
@@ -605,6 +605,7 @@ void splitk_stream_kernel(GemmParams p) {
         }
         if (at_tile >= 0) {
           const uint32_t old = __builtin_amdgcn_readfirstlane(at_old);
+          handoff_order();  // the partial loads stay after the arrival
           if (old == (uint32_t)(S - 1)) {
             if (lane == 0)
               __hip_atomic_store(cnt_of(at_tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -931,6 +932,7 @@ void splitk_stream_kernel(GemmParams p) {
       take = (old & kAbandon) != 0 && (old & kArrivals) == (uint32_t)(S - 1);
       if (take) __hip_atomic_store(cnt_of(tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    handoff_order();  // the partial loads of a taken tile stay after the arrival
     finish_mask(__builtin_amdgcn_ballot_w64(take), [&](int b) { return k0 + kstep * (j0 + b); }, false);
   }
 
@@ -983,6 +985,7 @@ void splitk_stream_kernel(GemmParams p) {
       __builtin_amdgcn_s_sleep(2);
     }
     if (ready) __hip_atomic_store(cnt_of(tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    handoff_order();  // the partial loads stay after the poll that saw every arrival
     finish_mask(__builtin_amdgcn_ballot_w64(ready), [&](int b) { return own_k(i0 + b); }, p.pdefer != 0);
   }
   write_stamps();
@@ -1163,15 +1166,17 @@ hipError_t launch_stream_fmt(int sh, const Tactic& t, const GemmParams& p, hipSt
   return hipErrorInvalidValue;
 }
 
-int env_int(const char* name, int dflt) {
-  const char* e = getenv(name);
-  return e ? atoi(e) : dflt;
-}
-
 // Fills the geometry of persistent shape `si`; false if it does not apply.
 bool stream_fits(int si, int T, int N, int ks, int S, int wf, Tactic* t, int L = 1) {
   const StreamShape& c = kStreamShapes[si];
   if (t->nt > kStreamMaxNT || ks == 0) return false;
+  // This kernel addresses all N weight rows (and their scales) through one
+  // buffer resource with 32-bit offsets: the span must stay below 2^31 bytes,
+  // where the out-of-range offset kOOB lies beyond every valid one. Larger
+  // weight matrices go to the kernels that rebase per tile.
+  const uint64_t K = (uint64_t)ks * (uint64_t)S;
+  if ((uint64_t)N * row_bytes(wf, (uint32_t)K) >= kOOB) return false;
+  if (wf != kBf16 && (uint64_t)N * (K / 32) >= kOOB) return false;
   // K elements per ring slot: one step of two pieces, or two one-piece steps.
   const int step = wf != kBf16 ? 2 * 4 * lane_k(wf) : 64;
   if (ks % step) return false;
@@ -1196,7 +1201,7 @@ bool stream_fits(int si, int T, int N, int ks, int S, int wf, Tactic* t, int L =
   // or faster on every decode and sweep shape, up to 40 % at T=24..32,
   // N=2048); batches keep the residency the LDS allows.
   if (L == 1) per_cu = 1;
-  per_cu = env_int("SKGEMM_WG_PER_CU", per_cu);
+  per_cu = knob(kKnobWgPerCu, per_cu);
   if (per_cu < 1) per_cu = 1;
   long g = ((long)kChipCUs * per_cu) / ((long)S * (L > 0 ? L : 1));  // the whole batch resident
   const long g_max = (n_tiles + c.wn - 1) / c.wn;  // every column gets a tile
@@ -1219,7 +1224,7 @@ bool stream_fits(int si, int T, int N, int ks, int S, int wf, Tactic* t, int L =
   // activation slice (single problems, waves sharing each tile, split K).
   t->pdefer = 0;
   if (L == 1 && S > 1 && c.wk > 1 && c.wn == 1 && c.mode != kStreamEpilogue &&
-      env_int("SKGEMM_PDEFER", 1) != 0) {
+      knob(kKnobPdefer, 1) != 0) {
     const long per_wg = (n_tiles + g - 1) / g;  // tiles of the busiest workgroup
     const long pl = per_wg * t->nt * 64 * 16;
     if (lds + pl <= kMaxLds) {
@@ -1240,13 +1245,13 @@ bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L) {
   const int ks = K / S;
   const int tr = T > 0 ? T : 1;
 
-  // SKGEMM_KIND=<0|1|2> restricts the choice to one kernel kind (tuning runs);
-  // SKGEMM_FOLD and SKGEMM_CLUSTER_C cap the fold and pin the pieces per lane
-  // of kind 2.
-  const int kind = env_int("SKGEMM_KIND", -1);
+  // A pinned kind (kKnobKind: tests and tuning runs) restricts the choice to
+  // that kernel kind; kKnobFold and kKnobClusterC cap the fold and pin the
+  // pieces per lane of kind 2.
+  const int kind = knob(kKnobKind, -1);
   if (kind == 2 || kind < 0) {
     Tactic c = t;
-    if (cluster_fits(tr, N, ks, S, wf, env_int("SKGEMM_FOLD", 8), env_int("SKGEMM_CLUSTER_C", 0), &c, L)) {
+    if (cluster_fits(tr, N, ks, S, wf, knob(kKnobFold, 8), knob(kKnobClusterC, 0), &c, L)) {
       // Whole tiles per workgroup pay off while the grid is about one
       // workgroup per CU; beyond, the persistent kernel's staged activations
       // and amortised ramp-up win. Every cluster workgroup re-reads all of X
@@ -1269,15 +1274,16 @@ bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L) {
     }
     if (kind == 2) return false;
   }
-  // Persistent streaming kernel (SKGEMM_STREAM=-1 disables it,
-  // SKGEMM_STREAM=<index> forces one of its shapes, for tuning runs).
+  // Persistent streaming kernel (a pinned kKnobStream forces one of its
+  // shapes, for tests and tuning runs).
   if (kind == 1 || kind < 0) {
-    const int forced = env_int("SKGEMM_STREAM", -2);
-    if (forced >= 0 && forced < kNumStreamShapes && stream_fits(forced, tr, N, ks, S, wf, &t, L)) {
-      *out = t;
-      return true;
-    }
-    if (forced == -2) {
+    const int forced = knob(kKnobStream, -1);
+    if (forced >= 0) {
+      if (forced < kNumStreamShapes && stream_fits(forced, tr, N, ks, S, wf, &t, L)) {
+        *out = t;
+        return true;
+      }
+    } else {
       // Eight waves share each tile's K slice (measured fastest on the decode
       // shapes: 16 weight rows open per workgroup, 8 streams on them); the
       // one-wave-per-tile shapes remain for when the slice is too short.
@@ -1331,10 +1337,9 @@ bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L) {
     }
     if (kind == 3) return false;
   }
-  // A tiled shape forced for tuning runs (SKGEMM_SHAPE=<index>), if it fits.
-  if (const char* e = getenv("SKGEMM_SHAPE")) {
-    const int si = atoi(e);
-    if (si >= 0 && si < kNumShapes && shape_fits(si, tr, N, ks, S, wf, &t)) {
+  // A tiled shape pinned for tests and tuning runs (kKnobShape), if it fits.
+  if (const int si = knob(kKnobShape, -1); si >= 0) {
+    if (si < kNumShapes && shape_fits(si, tr, N, ks, S, wf, &t)) {
       *out = t;
       return true;
     }

@@ -33,6 +33,24 @@ struct GemmParams {
   uint32_t bcnt;             // counters between problems' counters
 };
 
+// Choices the library normally makes itself, which tests and tuning runs can
+// pin through skgemm_set_override (include/skgemm.h lists their meanings).
+// knob() returns the pinned value, or dflt while the knob is unset. Nothing
+// else (no environment variable) changes which kernel a call runs.
+enum Knob {
+  kKnobKind = 0,     // kernel kind: 0 tiled, 1 persistent, 2 cluster, 3 wide
+  kKnobStream,       // persistent-kernel shape index
+  kKnobShape,        // tiled-kernel shape index
+  kKnobFold,         // largest fold of the cluster kernel
+  kKnobClusterC,     // 16-byte pieces per lane of bf16 cluster tiles
+  kKnobWgPerCu,      // persistent workgroups per CU the grid is sized for
+  kKnobPdefer,       // persistent kernel: partials held in LDS (1) or not (0)
+  kKnobOwnerWait,    // owner wait bound in device-clock ticks
+  kKnobHandoff,      // split-K hand-off of the persistent kernel: 0 counter, 1 mailbox
+  kKnobCount
+};
+int knob(int k, int dflt);
+
 // Words between the split-K arrival counters of two 16-row groups (one
 // 128-byte line per counter: the S ranks' arrivals and an owner's polls of
 // one tile then meet no other tile's at the device-scope atomic units).

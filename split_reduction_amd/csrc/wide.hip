@@ -313,6 +313,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
     return;
   }
   if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  handoff_order();  // the partial loads below stay after the arrivals were seen
 
   // Rank-order sum (this rank's partial from registers), one bf16 store per
   // quad. BATCH quads at a time keep BATCH * (S - 1) loads in flight.

@@ -30,3 +30,19 @@ def golden_rows(name):
                 continue
             rows.append(line.split())
     return rows
+
+
+@pytest.fixture
+def tune():
+    """Pins library choices through skgemm_set_override for one test
+    (``tune("kind", 1)``); every knob is restored to the library's own
+    choice afterwards."""
+    import split_reduction_amd as sk
+
+    def set_(name, value):
+        sk.skgemm_set_override(name, int(value))
+
+    try:
+        yield set_
+    finally:
+        sk.clear_overrides()

@@ -45,6 +45,25 @@ def empty_bf16(T: int, N: int):
     return t.empty((T, N), dtype=t.bfloat16, device=DEV)
 
 
+# A quiet-NaN bf16 pattern no kernel produces from finite inputs. Outputs are
+# filled with it before a call, so an element the call never wrote (a tile no
+# workgroup finished) cannot pass on a value left in memory by an earlier call.
+SENTINEL = 0x7FC1
+
+
+def sentinel_bf16(T: int, N: int):
+    t = torch()
+    return t.full((T, N), SENTINEL, dtype=t.int16, device=DEV).view(t.bfloat16)
+
+
+def checked_bits(C) -> np.ndarray:
+    """C's bits after a call; fails if any element still holds the sentinel."""
+    bits = bf16_bits(C)
+    left = int(np.count_nonzero(bits == SENTINEL))
+    assert left == 0, f"{left} output elements were never written"
+    return bits
+
+
 def run_bf16(x_bits, w_bits, split_k, W=None):
     """C bits from skgemm_bf16 on the given host operands."""
     import split_reduction_amd as sk
@@ -53,10 +72,10 @@ def run_bf16(x_bits, w_bits, split_k, W=None):
     N = w_bits.shape[0] if W is None else W.shape[0]
     X = to_dev_bf16(x_bits)
     W = to_dev_bf16(w_bits) if W is None else W
-    C = empty_bf16(T, N)
+    C = sentinel_bf16(T, N)
     sk.skgemm_bf16(W, X, C, T, N, K, split_k)
     torch().cuda.synchronize()
-    return bf16_bits(C)
+    return checked_bits(C)
 
 
 def run_mxfp4(x_bits, wq, ws, split_k):
@@ -67,10 +86,10 @@ def run_mxfp4(x_bits, wq, ws, split_k):
     X = to_dev_bf16(x_bits)
     Wq = to_dev_u8(wq)
     Ws = to_dev_u8(ws)
-    C = empty_bf16(T, N)
+    C = sentinel_bf16(T, N)
     sk.skgemm_mxfp4(Wq, Ws, X, C, T, N, K, split_k)
     torch().cuda.synchronize()
-    return bf16_bits(C)
+    return checked_bits(C)
 
 
 def assert_parity(c_bits, c_ref, K, what, rms=None):
@@ -92,7 +111,7 @@ def run_mxfp8(x_bits, wq8, ws, split_k):
     X = to_dev_bf16(x_bits)
     Wq = to_dev_u8(wq8)
     Ws = to_dev_u8(ws)
-    C = empty_bf16(T, N)
+    C = sentinel_bf16(T, N)
     sk.skgemm_mxfp8(Wq, Ws, X, C, T, N, K, split_k)
     torch().cuda.synchronize()
-    return bf16_bits(C)
+    return checked_bits(C)

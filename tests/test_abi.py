@@ -228,3 +228,59 @@ def test_tactic_rules(T, N, K, S, wf, want):
     assert got == want, (T, N, K, S, wf, t)
     if t["kind"] == "cluster":
         assert t["wk"] <= 8
+
+
+def _row_bytes(wf, K):
+    return K // 2 if wf == 1 else K if wf == 2 else 2 * K
+
+
+@pytest.mark.parametrize("T,N,K,S,wf", [
+    (1, 262144, 16384, 8, 0),     # 8 GiB of bf16 weights
+    (8, 131072, 8192, 4, 0),      # exactly 2 GiB
+    (8, 65536, 16384, 8, 0),      # exactly 2 GiB
+    (16, 262144, 32768, 4, 1),    # MXFP4, 4 GiB of codes
+    (32, 262144, 16384, 8, 2),    # MXFP8, 4 GiB of codes
+    (1, 16384, 16384, 8, 0),      # 512 MiB: the persistent kernel
+])
+def test_weight_span_fits_the_chosen_kernel(T, N, K, S, wf):
+    """A kernel that addresses the whole weight matrix through one buffer
+    resource (the persistent kernel) is chosen only while that span stays
+    below 2^31 bytes; larger matrices go to kernels that rebase the resource
+    per tile, and the call is still accepted."""
+    _ensure_built()
+    t = sk.skgemm_tactic_for(T, N, K, S, wf)
+    span = N * _row_bytes(wf, K)
+    if t["kind"] == "stream":
+        assert span < 2**31 and (wf == 0 or N * (K // 32) < 2**31)
+    else:
+        # per-tile resources: at most 256 rows of one tile
+        assert t["tile_n"] * _row_bytes(wf, K) <= 2**31
+    if span >= 2**31:
+        assert t["kind"] != "stream"
+
+
+def test_override_pins_and_restores():
+    """skgemm_set_override pins a choice for later calls and the tactic
+    query; -1 restores the library's own choice; bad knobs and values are
+    rejected. No environment variable changes the choice."""
+    _ensure_built()
+    lib = sk.lib()
+    own = sk.skgemm_tactic_for(8, 2048, 7168, 4)
+    assert own["kind"] == "cluster"
+    os.environ["SKGEMM_KIND"] = "1"  # ignored: only the override pins a kind
+    try:
+        assert sk.skgemm_tactic_for(8, 2048, 7168, 4) == own
+        sk.skgemm_set_override("kind", 1)
+        assert sk.skgemm_tactic_for(8, 2048, 7168, 4)["kind"] == "stream"
+        sk.skgemm_set_override("kind", 3)  # the wide kernel cannot take T = 8
+        with pytest.raises(sk.SkgemmError) as e:
+            sk.skgemm_tactic_for(8, 2048, 7168, 4)
+        assert e.value.code == sk.SKGEMM_ESHAPE
+        sk.skgemm_set_override("kind", -1)
+        assert sk.skgemm_tactic_for(8, 2048, 7168, 4) == own
+    finally:
+        os.environ.pop("SKGEMM_KIND", None)
+        sk.clear_overrides()
+    assert lib.skgemm_set_override(99, 0) == sk.SKGEMM_EINVAL
+    assert lib.skgemm_set_override(-1, 0) == sk.SKGEMM_EINVAL
+    assert lib.skgemm_set_override(0, -2) == sk.SKGEMM_EINVAL

@@ -88,3 +88,113 @@ def test_excluding_the_owners_workgroup_loses_a_tile():
         order = tuple(range(1, S)) + (0,)  # the owner's own arrival last
         assert run(order, S - 1, S, 0, take_not_owner) == []
         assert run(order, S - 1, S, 0, take_any) == [("arrival", 0)]
+
+
+# ---------------------------------------------------------------------------
+# Partials held in LDS (persistent kernel, pdefer): the owner's own partial
+# is never stored unless the owner gives up. Its give-up must store that
+# partial and wait for the stores to complete *before* the abandon bit is
+# set, or the rank that takes the tile over could sum a partial that is not
+# there yet.
+# ---------------------------------------------------------------------------
+
+
+def run_pdefer(order, give_up_at, S, owner, store_first):
+    """Finisher and the partials it could see. Peers store, wait for their
+    stores, then arrive; the owner's own arrival is made by another wave of its
+    workgroup (its partial stays in LDS). At give_up_at the owner gives up:
+    with store_first it stores its held partial (complete) and then sets the
+    abandon bit; otherwise the abandon bit goes first and the store lands one
+    event later."""
+    cnt = 0
+    visible = set()
+    result = []
+    pending_store = False
+    events = list(order)
+    for pos in range(S + 1):
+        if pending_store:  # the owner's late store lands now
+            visible.add(owner)
+            pending_store = False
+        if pos == give_up_at:
+            if store_first:
+                visible.add(owner)
+            old, cnt = cnt, cnt | ABANDON
+            if not store_first:
+                pending_store = True
+            if (old & ARRIVALS) == S:
+                result.append(("owner", set(range(S))))  # the owner sums its own from LDS
+        if pos < S:
+            rank = events[pos]
+            if rank != owner:
+                visible.add(rank)  # a peer's stores complete before its arrival
+            old, cnt = cnt, cnt + 1
+            if take_any(old, S, rank, owner):
+                result.append((("arrival", rank), set(visible)))
+    return result
+
+
+def test_pdefer_give_up_stores_before_abandon():
+    for S in (2, 4, 8):
+        for order, give_up_at, owner in scenarios(S):
+            res = run_pdefer(order, give_up_at, S, owner, store_first=True)
+            assert len(res) == 1, (S, order, give_up_at, res)
+            who, seen = res[0]
+            assert seen == set(range(S)), (S, order, give_up_at, who, seen)
+
+
+def test_pdefer_abandon_before_store_loses_a_partial():
+    """The planted wrong order: the abandon bit set before the owner's held
+    partial is stored. Some order then lets the take-over sum without it."""
+    bad = 0
+    for S in (2, 4):
+        for order, give_up_at, owner in scenarios(S):
+            for who, seen in run_pdefer(order, give_up_at, S, owner, store_first=False):
+                if who != "owner" and owner not in seen:
+                    bad += 1
+    assert bad > 0
+
+
+# ---------------------------------------------------------------------------
+# Wide kernel: each wave column's owner makes its own arrival first, then
+# waits (bounded) and may give up; peers only arrive. Every interleaving of
+# the owner's arrival, its optional give-up after it, and the peers' arrivals
+# must leave exactly one finisher.
+# ---------------------------------------------------------------------------
+
+
+def run_wide(order, give_up_after, S, owner):
+    """order: the S arrivals in time order (the owner's among them);
+    give_up_after: number of arrivals after which the owner gives up (None:
+    never; it must come after the owner's own arrival)."""
+    cnt = 0
+    finishers = []
+    owner_done = False
+    owner_arrived = False
+    for pos in range(S + 1):
+        if give_up_after is not None and pos == give_up_after and owner_arrived and not owner_done:
+            old, cnt = cnt, cnt | ABANDON
+            if (old & ARRIVALS) == S:
+                finishers.append("owner")
+            owner_done = True
+        if pos < S:
+            rank = order[pos]
+            old, cnt = cnt, cnt + 1
+            if rank == owner:
+                owner_arrived = True
+                if (old & ARRIVALS) == S - 1:  # the others were all here already
+                    finishers.append("owner")
+                    owner_done = True
+            elif (old & ABANDON) and (old & ARRIVALS) == S - 1:
+                finishers.append(("arrival", rank))
+    if not owner_done and (cnt & ARRIVALS) == S:
+        finishers.append("owner")  # the poll sees all S arrivals
+    return finishers
+
+
+def test_wide_owner_arrives_first_exactly_one_finisher():
+    for S in (2, 3, 4, 8):
+        for order, _, owner in scenarios(S):
+            p_owner = order.index(owner)
+            for give_up_after in [None] + list(range(p_owner + 1, S + 1)):
+                f = run_wide(order, give_up_after, S, owner)
+                assert len(f) == 1, (S, order, give_up_after, f)
