@@ -60,7 +60,9 @@ enum skgemm_status {
                          (MXFP4) non-zero, or a size above the limits below   */
   SKGEMM_ENOMEM = -4, /* split-K workspace could not be allocated, or it would
                          have to grow while the stream is being captured      */
-  SKGEMM_EHIP = -5    /* a HIP runtime call failed; see skgemm_last_hip_error */
+  SKGEMM_EHIP = -5,   /* a HIP runtime call failed; see skgemm_last_hip_error */
+  SKGEMM_ESCRATCH = -6 /* skgemm_bf16_noalloc: the call needs more split-K
+                          partials than its fixed scratch holds              */
 };
 
 /* Size limits (checked; SKGEMM_ESHAPE beyond them). T has no upper limit:
@@ -84,6 +86,31 @@ enum skgemm_status {
  */
 SKGEMM_API int skgemm_bf16(const void* W, const void* X, void* C, int T, int N, int K,
                            int split_k, hipStream_t stream);
+
+/*
+ * skgemm_bf16_noalloc: skgemm_bf16 for callers that cannot allocate device
+ * memory -- code under HIP graph capture without a prior skgemm_reserve,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * kernels and results (bit for bit) as skgemm_bf16, but the split-K
+ * partials and counters live in a fixed scratch array of
+ * SKGEMM_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; this call never allocates or frees memory.
+ *   Limit: with split_k > 1, split_k * min(T, 128) * N * 4 bytes of partials
+ *   must fit in SKGEMM_NOALLOC_SCRATCH_BYTES - SKGEMM_NOALLOC_PART_OFFSET
+ *   (39.8 MB: e.g. T = 128, N = 16384 at split_k = 4); larger calls return
+ *   SKGEMM_ESCRATCH before any device work. split_k = 1 needs no scratch.
+ *   Every call on one GPU shares that GPU's scratch, from any stream: calls
+ *   that may overlap in time (other streams, other threads) race and give
+ *   wrong results; order them (one stream, or events). The counter area is
+ *   cleared on the device's first calls (a fill kernel enqueued on `stream`;
+ *   inside a graph capture the clear is captured too) and every call leaves
+ *   it zeroed. Time-outs of the bounded owner wait are not reported by
+ *   skgemm_health for this entry point.
+ */
+#define SKGEMM_NOALLOC_SCRATCH_BYTES ((size_t)40 << 20)
+#define SKGEMM_NOALLOC_PART_OFFSET ((size_t)(2 << 20) + 4096)
+SKGEMM_API int skgemm_bf16_noalloc(const void* W, const void* X, void* C, int T, int N, int K,
+                                   int split_k, hipStream_t stream);
 
 /*
  * skgemm_mxfp4: C = X . dequant(Wq, Wscale)^T. The weights are decoded exactly

@@ -25,6 +25,7 @@ SKGEMM_EALIGN = -2
 SKGEMM_ESHAPE = -3
 SKGEMM_ENOMEM = -4
 SKGEMM_EHIP = -5
+SKGEMM_ESCRATCH = -6
 
 # skgemm_set_override knobs (include/skgemm.h, enum skgemm_knob)
 KNOBS = {"kind": 0, "stream": 1, "shape": 2, "fold": 3, "cluster_c": 4, "wg_per_cu": 5,
@@ -62,6 +63,7 @@ def _declare(lib):
         "skgemm_read_probe": [vp, sz, vp, st],
         "skgemm_health": [vp, sz, st],
         "skgemm_set_override": [i, i],
+        "skgemm_bf16_noalloc": [vp, vp, vp, i, i, i, i, st],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -161,6 +163,14 @@ def skgemm_bf16(W, X, C, T: int, N: int, K: int, split_k: int, stream=None) -> N
     code = lib().skgemm_bf16(_ptr(W, 2 * _n(N, K), "W"), _ptr(X, 2 * _n(T, K), "X"),
                              _ptr(C, 2 * _n(T, N), "C"), T, N, K, split_k, _stream(stream))
     _check(code, "skgemm_bf16")
+
+
+def skgemm_bf16_noalloc(W, X, C, T: int, N: int, K: int, split_k: int, stream=None) -> None:
+    """skgemm_bf16 with the split-K workspace in the library's fixed per-GPU
+    scratch: allocates nothing (SKGEMM_ESCRATCH when the call needs more)."""
+    code = lib().skgemm_bf16_noalloc(_ptr(W, 2 * _n(N, K), "W"), _ptr(X, 2 * _n(T, K), "X"),
+                                     _ptr(C, 2 * _n(T, N), "C"), T, N, K, split_k, _stream(stream))
+    _check(code, "skgemm_bf16_noalloc")
 
 
 def skgemm_mxfp4(Wq, Wscale, X, C, T: int, N: int, K: int, split_k: int, stream=None) -> None:

@@ -158,8 +158,11 @@ int check_batch(const Batch& b, int T, int N) {
   return SKGEMM_OK;
 }
 
+// `given`: a workspace the caller provides (the no-allocation entry point's
+// fixed scratch); calls that need more than it holds get SKGEMM_ESCRATCH.
+// Without it the stream's own workspace is used (allocated or grown here).
 int run_gemm(int wf, const void* w, const void* ws, const void* x, void* c, int T, int N, int K,
-             int S, hipStream_t stream, const Batch& batch = Batch{}) {
+             int S, hipStream_t stream, const Batch& batch = Batch{}, const Workspace* given = nullptr) {
   int rc = check_gemm(wf, w, ws, x, c, T, N, K, S, true);
   if (rc != SKGEMM_OK) return rc;
   rc = check_batch(batch, T, N);
@@ -168,8 +171,14 @@ int run_gemm(int wf, const void* w, const void* ws, const void* x, void* c, int 
   const int L = batch.L;
   Workspace wsp;
   if (S > 1) {
-    rc = ensure_workspace(stream, part_bytes_for(T, N, S) * (size_t)L, counters_for(N) * (size_t)L, &wsp);
-    if (rc != SKGEMM_OK) return rc;
+    const size_t part = part_bytes_for(T, N, S) * (size_t)L, cnts = counters_for(N) * (size_t)L;
+    if (given != nullptr) {
+      if (part > given->part_bytes || cnts > given->cnt_count) return SKGEMM_ESCRATCH;
+      wsp = *given;
+    } else {
+      rc = ensure_workspace(stream, part, cnts, &wsp);
+      if (rc != SKGEMM_OK) return rc;
+    }
   }
   const int cus = device_cus();
   for (int t0 = 0; t0 < T; t0 += kTokenBlock) {
@@ -211,6 +220,64 @@ int run_gemm(int wf, const void* w, const void* ws, const void* x, void* c, int 
   return SKGEMM_OK;
 }
 
+// ---- the fixed scratch of skgemm_bf16_noalloc -----------------------------
+// One array per GPU, held until the process ends: arrival counters for the
+// largest N (one 128-byte line per 16 output rows) and the health words at
+// the front, FP32 partials after them. In host code `scratch` names a host
+// stand-in, not device memory: every use goes through the device address
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchCounterWords = (size_t)SKGEMM_MAX_N / 16 * skg::kCntStride;
+constexpr size_t kScratchPartOffset = SKGEMM_NOALLOC_PART_OFFSET;
+static_assert(kScratchCounterWords * 4 + skg::kHealthWords * 4 <= kScratchPartOffset,
+              "counters and health words fit before the partials");
+static_assert(kScratchPartOffset % 256 == 0 && SKGEMM_NOALLOC_SCRATCH_BYTES > kScratchPartOffset,
+              "partials start on a 256-byte boundary inside the scratch");
+
+static __device__ __align__(256) uint8_t scratch[SKGEMM_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchState {
+  uint8_t* ptr = nullptr;  // device address of this GPU's copy of `scratch`
+  bool zeroed = false;     // its counter area was cleared outside graph capture
+};
+std::mutex g_scratch_mu;
+std::map<int, ScratchState> g_scratch;
+
+// The current device's scratch as a workspace. At the first call on a device
+// its address is looked up; until one call has cleared the counter area
+// outside graph capture, each call first enqueues that clear (a fill kernel,
+// no memset node in a captured graph); the first uncaptured clear is waited
+// for, so calls on other streams start from zeroed counters.
+int noalloc_workspace(hipStream_t stream, Workspace* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchState& st = g_scratch[dev];
+  if (st.ptr == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    st.ptr = static_cast<uint8_t*>(ptr);
+  }
+  if (!st.zeroed) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return hip_fail(e);
+    e = skg::launch_zero16(st.ptr, kScratchPartOffset, stream);
+    if (e != hipSuccess) return hip_fail(e);
+    if (cap == hipStreamCaptureStatusNone) {
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e);
+      st.zeroed = true;
+    }
+  }
+  out->cnt = reinterpret_cast<uint32_t*>(st.ptr);
+  out->cnt_count = kScratchCounterWords;
+  out->part = reinterpret_cast<float*>(st.ptr + kScratchPartOffset);
+  out->part_bytes = SKGEMM_NOALLOC_SCRATCH_BYTES - kScratchPartOffset;
+  return SKGEMM_OK;
+}
+
 }  // namespace
 
 int skg::knob(int k, int dflt) {
@@ -224,6 +291,23 @@ extern "C" {
 SKGEMM_API int skgemm_bf16(const void* W, const void* X, void* C, int T, int N, int K,
                            int split_k, hipStream_t stream) {
   return run_gemm(skg::kBf16, W, nullptr, X, C, T, N, K, split_k, stream);
+}
+
+SKGEMM_API int skgemm_bf16_noalloc(const void* W, const void* X, void* C, int T, int N, int K,
+                                   int split_k, hipStream_t stream) {
+  // Shape checks first: a call the scratch cannot serve fails before any
+  // device work (the same checks run_gemm repeats).
+  int rc = check_gemm(skg::kBf16, W, nullptr, X, C, T, N, K, split_k, true);
+  if (rc != SKGEMM_OK) return rc;
+  if (T == 0 || N == 0) return SKGEMM_OK;
+  if (split_k > 1 && part_bytes_for(T, N, split_k) > SKGEMM_NOALLOC_SCRATCH_BYTES - kScratchPartOffset)
+    return SKGEMM_ESCRATCH;
+  Workspace w;
+  if (split_k > 1) {
+    rc = noalloc_workspace(stream, &w);
+    if (rc != SKGEMM_OK) return rc;
+  }
+  return run_gemm(skg::kBf16, W, nullptr, X, C, T, N, K, split_k, stream, Batch{}, &w);
 }
 
 SKGEMM_API int skgemm_mxfp4(const void* Wq, const void* Wscale, const void* X, void* C, int T,
@@ -435,6 +519,7 @@ SKGEMM_API const char* skgemm_strerror(int code) {
     case SKGEMM_ESHAPE: return "unsupported shape (N % 16, K % (32*split_k) or K % (128*split_k) for MXFP4, or size limit)";
     case SKGEMM_ENOMEM: return "split-K workspace could not be allocated (or must grow during stream capture: call skgemm_reserve first)";
     case SKGEMM_EHIP: return "HIP runtime error (see skgemm_last_hip_error)";
+    case SKGEMM_ESCRATCH: return "the call needs more split-K partials than the fixed scratch of skgemm_bf16_noalloc holds (split_k * min(T,128) * N * 4 bytes; see SKGEMM_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown skgemm status";
 }

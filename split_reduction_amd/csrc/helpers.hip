@@ -79,6 +79,21 @@ unsigned blocks_for(size_t n, size_t per_block) {
 
 }  // namespace
 
+// Zeros n 16-byte pieces with vector stores: the set-up clear of a counter
+// area, as a kernel so that a graph that captures it holds no memset node.
+__global__ __launch_bounds__(kThreads) void zero16_kernel(u32x4* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_zero16(void* p, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 16;
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = blocks_for(n, kThreads) < 1024u ? blocks_for(n, kThreads) : 1024u;
+  hipLaunchKernelGGL(zero16_kernel, dim3(blocks), dim3(kThreads), 0, s, static_cast<u32x4*>(p), n);
+  return hipGetLastError();
+}
+
 hipError_t launch_pack_bf16(const float* in, uint32_t* out, size_t n, hipStream_t s) {
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(pack_bf16_kernel, dim3(blocks_for(n, kThreads)), dim3(kThreads), 0, s, in,

@@ -141,6 +141,9 @@ hipError_t launch_wide(const Tactic& t, const GemmParams& p, hipStream_t stream)
 // Enqueues one launch (T <= 128). Returns the launch's hipError_t.
 hipError_t launch_gemm(const Tactic& tac, const GemmParams& p, hipStream_t stream);
 
+// Zeros `bytes` (a multiple of 16, 16-byte aligned) with a fill kernel.
+hipError_t launch_zero16(void* p, size_t bytes, hipStream_t s);
+
 // Test and helper kernels (bit-exact checks of the device helpers).
 hipError_t launch_pack_bf16(const float* in, uint32_t* out, size_t n_pairs, hipStream_t s);
 hipError_t launch_pack_e4m3(const float* in, uint32_t* out, size_t n_quads, hipStream_t s);

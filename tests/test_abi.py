@@ -149,7 +149,7 @@ def test_binding_rejects_tensors_it_cannot_pass():
 
 def test_strerror_covers_every_code():
     _ensure_built()
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert sk.strerror(code) and "unknown" not in sk.strerror(code)
     assert "unknown" in sk.strerror(-99)
 
