@@ -88,6 +88,22 @@ SKGEMM_API int skgemm_bf16(const void* W, const void* X, void* C, int T, int N, 
                            int split_k, hipStream_t stream);
 
 /*
+ * skgemm_bf16_e4m3: skgemm_bf16 with an 8-bit output: C8[t, n] is the OCP
+ * E4M3FN code of min(max(sum * c_scale, -448), 448), rounded to nearest even,
+ * where sum is the same FP32 rank-order sum skgemm_bf16 rounds to bf16 (the
+ * E4M3 packing of page vllm.models.deepseek_v41.amd.mono.common.ops,
+ * fp8_pack4, on values brought into its range by the scale and a
+ * saturation). The product with c_scale is one FP32 multiply.
+ *   C8       uint8 [T, N] row-major, device memory, 16-byte aligned.
+ *   c_scale  finite and > 0 (SKGEMM_EINVAL otherwise); typically 448 over
+ *            the largest |C| expected, or a power of two.
+ *   Other arguments, limits and errors as skgemm_bf16. Non-finite sums are
+ *   outside the contract.
+ */
+SKGEMM_API int skgemm_bf16_e4m3(const void* W, const void* X, void* C8, float c_scale, int T, int N,
+                                int K, int split_k, hipStream_t stream);
+
+/*
  * skgemm_bf16_noalloc: skgemm_bf16 for callers that cannot allocate device
  * memory -- code under HIP graph capture without a prior skgemm_reserve,
  * tight serving loops, harnesses that forbid hipMalloc. Same arguments,

@@ -147,6 +147,31 @@ def f32_to_e4m3_rne(x) -> np.ndarray:
     return (c | np.where(sign, 0x80, 0)).astype(np.uint8)
 
 
+def e4m3_rne_sat(x) -> np.ndarray:
+    """float64 values -> E4M3FN codes (uint8) of the values saturated to the
+    format's range: each value is first clamped to [-448, 448] (448 is the
+    largest finite E4M3FN magnitude), then rounded to the nearest of the 127
+    non-negative finite magnitudes, ties to the even code, with the sign in
+    bit 7 (-0.0 gives 0x80). This is the output stage of the E4M3-output
+    GEMM: the pages' ``fp8_pack4`` packs values "already in range", and the
+    saturation is what brings a scaled sum into that range. NaN is rejected.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.isnan(x)):
+        raise ValueError("E4M3 output of NaN is outside the contract")
+    y = np.clip(x, -E4M3_MAX, E4M3_MAX)
+    codes = np.arange(0x7F, dtype=np.int64)
+    mags = e4m3_value(codes)
+    a = np.abs(y)
+    hi = np.minimum(np.searchsorted(mags, a, side="left"), len(mags) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = np.abs(a - mags[lo])
+    d_hi = np.abs(mags[hi] - a)
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((codes[hi] & 1) == 0))
+    c = np.where(take_hi, codes[hi], codes[lo])
+    return (c | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
 def e4m3_pack4_word(a, b, c, d) -> np.ndarray:
     """Four float32 (in range) -> one uint32 of E4M3 bytes a, b, c, d, low first.
 

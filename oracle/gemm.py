@@ -29,7 +29,7 @@ import math
 
 import numpy as np
 
-from .formats import bf16_bits_to_f64, mxfp4_dequant_f64, mxfp8_dequant_f64
+from .formats import E4M3_MAX, bf16_bits_to_f64, e4m3_rne_sat, e4m3_value, mxfp4_dequant_f64, mxfp8_dequant_f64
 
 
 def gemm_decoded_ref(x_bits: np.ndarray, w: np.ndarray) -> np.ndarray:
@@ -113,6 +113,48 @@ def violation_ratio(c_test: np.ndarray, c_ref: np.ndarray, k: int, rms=None) -> 
     with np.errstate(divide="ignore", invalid="ignore"):
         r = np.where(err == 0, 0.0, err / bound)
     return float(np.max(r))
+
+
+# ---------------------------------------------------------------------------
+# E4M3 output
+# ---------------------------------------------------------------------------
+
+
+def gemm_bf16_e4m3_ref(x_bits: np.ndarray, w_bits: np.ndarray, c_scale: float):
+    """The E4M3-output GEMM: y = clamp(c_scale * X . W^T, -448, 448) in
+    float64 (not rounded) and the codes of y, rounded to nearest even
+    (``formats.e4m3_rne_sat``). Returns (y, codes)."""
+    y = np.clip(gemm_bf16_ref(x_bits, w_bits) * float(c_scale), -E4M3_MAX, E4M3_MAX)
+    return y, e4m3_rne_sat(y)
+
+
+def e4m3_out_violation_ratio(codes: np.ndarray, ref: np.ndarray, k: int, c_scale: float, rms=None) -> float:
+    """max |E4M3(code) - y| / bound over the output (<= 1 passes), with
+    y = clamp(c_scale * ref, -448, 448) and
+
+        bound = 2**-4 |y| + 2**-10 + (1 + 2**-4) * c_scale * 1e-3 * sqrt(K) * rms(ref).
+
+    Where the kernel's FP32 value is v = c_scale * (ref + e) with |e| within
+    the bf16 output's accumulation term 1e-3 sqrt(K) rms(ref) (the scale
+    multiply adds one rounding of 2**-24 relative, far below it), saturation
+    to [-448, 448] moves v and y by no more than |v - y|, and round to nearest
+    E4M3 adds at most half a unit in the last place: 2**-4 of the magnitude
+    for normal values (3 mantissa bits), 2**-10 below 2**-6 (subnormal step
+    2**-9). Summed: |E4M3 - y| <= 2**-4 (|y| + |v - y|) + 2**-10 + |v - y|.
+    NaN codes count as failures."""
+    vals = e4m3_value(np.asarray(codes))
+    ref = np.asarray(ref, dtype=np.float64)
+    if vals.shape != ref.shape:
+        raise ValueError(f"shape mismatch {vals.shape} vs {ref.shape}")
+    if ref.size == 0:
+        return 0.0
+    if np.any(np.isnan(vals)):
+        return math.inf
+    if rms is None:
+        rms = math.sqrt(float(np.mean(ref * ref)))
+    y = np.clip(ref * float(c_scale), -E4M3_MAX, E4M3_MAX)
+    bound = 2.0**-4 * np.abs(y) + 2.0**-10 + (1 + 2.0**-4) * float(c_scale) * 1e-3 * math.sqrt(k) * rms
+    return float(np.max(np.abs(vals - y) / bound))
 
 
 # ---------------------------------------------------------------------------

@@ -64,6 +64,7 @@ def _declare(lib):
         "skgemm_health": [vp, sz, st],
         "skgemm_set_override": [i, i],
         "skgemm_bf16_noalloc": [vp, vp, vp, i, i, i, i, st],
+        "skgemm_bf16_e4m3": [vp, vp, vp, ctypes.c_float, i, i, i, i, st],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -163,6 +164,13 @@ def skgemm_bf16(W, X, C, T: int, N: int, K: int, split_k: int, stream=None) -> N
     code = lib().skgemm_bf16(_ptr(W, 2 * _n(N, K), "W"), _ptr(X, 2 * _n(T, K), "X"),
                              _ptr(C, 2 * _n(T, N), "C"), T, N, K, split_k, _stream(stream))
     _check(code, "skgemm_bf16")
+
+
+def skgemm_bf16_e4m3(W, X, C8, c_scale: float, T: int, N: int, K: int, split_k: int, stream=None) -> None:
+    """C8[T, N] (uint8 E4M3FN codes) of (X . W^T) * c_scale, saturated to +-448."""
+    code = lib().skgemm_bf16_e4m3(_ptr(W, 2 * _n(N, K), "W"), _ptr(X, 2 * _n(T, K), "X"),
+                                  _ptr(C8, _n(T, N), "C8"), float(c_scale), T, N, K, split_k, _stream(stream))
+    _check(code, "skgemm_bf16_e4m3")
 
 
 def skgemm_bf16_noalloc(W, X, C, T: int, N: int, K: int, split_k: int, stream=None) -> None:

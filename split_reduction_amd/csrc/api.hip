@@ -161,8 +161,15 @@ int check_batch(const Batch& b, int T, int N) {
 // `given`: a workspace the caller provides (the no-allocation entry point's
 // fixed scratch); calls that need more than it holds get SKGEMM_ESCRATCH.
 // Without it the stream's own workspace is used (allocated or grown here).
+// Output format of a call: bf16, or E4M3FN bytes of sum * c_scale (saturated).
+struct OutFmt {
+  int e4m3 = 0;
+  float c_scale = 1.0f;
+};
+
 int run_gemm(int wf, const void* w, const void* ws, const void* x, void* c, int T, int N, int K,
-             int S, hipStream_t stream, const Batch& batch = Batch{}, const Workspace* given = nullptr) {
+             int S, hipStream_t stream, const Batch& batch = Batch{}, const Workspace* given = nullptr,
+             const OutFmt& out = OutFmt{}) {
   int rc = check_gemm(wf, w, ws, x, c, T, N, K, S, true);
   if (rc != SKGEMM_OK) return rc;
   rc = check_batch(batch, T, N);
@@ -189,7 +196,9 @@ int run_gemm(int wf, const void* w, const void* ws, const void* x, void* c, int 
     p.w = w;
     p.wscale = static_cast<const uint8_t*>(ws);
     p.x = static_cast<const uint8_t*>(x) + (size_t)t0 * (size_t)K * 2;
-    p.c = static_cast<uint8_t*>(c) + (size_t)t0 * (size_t)N * 2;
+    p.c = static_cast<uint8_t*>(c) + (size_t)t0 * (size_t)N * (out.e4m3 ? 1 : 2);
+    p.out_e4m3 = out.e4m3;
+    p.c_scale = out.c_scale;
     p.part = wsp.part;
     p.cnt = wsp.cnt;
     p.T = tb;
@@ -291,6 +300,15 @@ extern "C" {
 SKGEMM_API int skgemm_bf16(const void* W, const void* X, void* C, int T, int N, int K,
                            int split_k, hipStream_t stream) {
   return run_gemm(skg::kBf16, W, nullptr, X, C, T, N, K, split_k, stream);
+}
+
+SKGEMM_API int skgemm_bf16_e4m3(const void* W, const void* X, void* C8, float c_scale, int T, int N,
+                                int K, int split_k, hipStream_t stream) {
+  if (!(c_scale > 0.0f) || !(c_scale < 3.0e38f)) return SKGEMM_EINVAL;  // finite, positive (NaN fails)
+  OutFmt out;
+  out.e4m3 = 1;
+  out.c_scale = c_scale;
+  return run_gemm(skg::kBf16, W, nullptr, X, C8, T, N, K, split_k, stream, Batch{}, nullptr, out);
 }
 
 SKGEMM_API int skgemm_bf16_noalloc(const void* W, const void* X, void* C, int T, int N, int K,

@@ -36,6 +36,7 @@
 // are transposed across lane rows to match). See the notes at each.
 
 #include "device/mfma.h"
+#include "device/out.h"
 #include "device/pack.h"
 #include "device/types.h"
 #include "device/wfmt.h"
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
   const rsrc_t sr = MX ? make_rsrc(p.wscale + (size_t)n0 * (K / 32), (uint32_t)R * (uint32_t)(K / 32))
                        : wr;
   const rsrc_t xr = make_rsrc(p.x, (uint32_t)T * (uint32_t)K * 2u);
-  const rsrc_t cr = make_rsrc(p.c, (uint32_t)T * (uint32_t)N * 2u);
+  const COut co = make_cout(p);
 
   // Byte offsets that do not change with the step.
   const uint32_t a_row = LINES ? line_pair_offset(li, 0, wrow_bytes) : (uint32_t)ra * wrow_bytes;
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
         v0 += part[(rk * 32 + t) * 16 + r];
         v1 += part[(rk * 32 + t) * 16 + r + 1];
       }
-      st4_if(true, bf16_pair(v0, v1), cr, ((uint32_t)t * (uint32_t)N + (uint32_t)(n0 + r)) * 2u);
+      store_pair(co, true, v0, v1, (uint32_t)t * (uint32_t)N + (uint32_t)(n0 + r));
     }
   };
   auto reduce = [&](auto s_c) {
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
         v0 += part[(rk * 32 + t) * 16 + r];
         v1 += part[(rk * 32 + t) * 16 + r + 1];
       }
-      st4_if(true, bf16_pair(v0, v1), cr, ((uint32_t)t * (uint32_t)N + (uint32_t)(n0 + r)) * 2u);
+      store_pair(co, true, v0, v1, (uint32_t)t * (uint32_t)N + (uint32_t)(n0 + r));
     }
   };
   if constexpr (F <= 2) {

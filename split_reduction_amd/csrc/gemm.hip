@@ -39,6 +39,7 @@
 //    which leaves the contraction unchanged.
 
 #include "device/mfma.h"
+#include "device/out.h"
 #include "device/pack.h"
 #include "device/types.h"
 #include "device/wfmt.h"
@@ -280,9 +281,9 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
 
   const bool owner = (wk == 0);
   const int n_lane = n0 + wn * RG * 16 + 4 * g;  // feature of quad element 0, rg = 0
-  const rsrc_t cr = make_rsrc(p.c, (uint32_t)T * (uint32_t)N * 2u);
-  auto c_off = [&](int rg, int tt) -> uint32_t {
-    return ((uint32_t)(tt * 16 + li) * (uint32_t)N + (uint32_t)(n_lane + rg * 16)) * 2u;
+  const COut co = make_cout(p);
+  auto c_el = [&](int rg, int tt) -> uint32_t {
+    return (uint32_t)(tt * 16 + li) * (uint32_t)N + (uint32_t)(n_lane + rg * 16);
   };
   auto in_t = [&](int tt) -> bool { return owner && (tt * 16 + li < T); };
 
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) st8_if(in_t(tt), bf16_quad(acc[rg][tt]), cr, c_off(rg, tt));
+      for (int tt = 0; tt < NT; ++tt) store_quad(co, in_t(tt), acc[rg][tt], c_el(rg, tt));
     return;
   }
 
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
       for (int r = 1; r < 8; ++r) {
         if (r < S) tot += (r == rank) ? acc[rg][tt] : v[r];
       }
-      st8_if(ok, bf16_quad(tot), cr, c_off(rg, tt));
+      store_quad(co, ok, tot, c_el(rg, tt));
     }
   }
 }
@@ -453,7 +454,7 @@ void splitk_stream_kernel(GemmParams p) {
   const rsrc_t wr = make_rsrc(p.w, (uint32_t)N * wrow_bytes);
   const rsrc_t sr = MX ? make_rsrc(p.wscale, (uint32_t)N * (uint32_t)(K / 32)) : wr;
   const rsrc_t xr = make_rsrc(p.x, (uint32_t)T * (uint32_t)K * 2u);
-  const rsrc_t cr = make_rsrc(p.c, (uint32_t)T * (uint32_t)N * 2u);
+  const COut co = make_cout(p);
   const rsrc_t pr = make_rsrc(p.part, (uint32_t)S * (uint32_t)T * (uint32_t)N * 4u);
   // Arrival counter of a 16-row tile: one 128-byte line each, so the S
   // ranks' arrivals and the owner's polls of one tile meet no other tile's
@@ -500,15 +501,23 @@ void splitk_stream_kernel(GemmParams p) {
   };
 
   // ---- stage this rank's X slice once ------------------------------------
-  // The weight prologue goes out only once the slice is in LDS: issued
-  // together, the two share the CU's intake and the slice, which every
-  // multiply waits for, lands late (measured 0.3-2 us slower per launch).
+  // The first XPRE loads per thread of the slice go out first, then the
+  // weight prologue, then the slice's LDS writes. Loads complete in order for
+  // the wait counter, so the writes wait only for the older activation loads
+  // while the first ring slots of weights arrive behind them: the weight
+  // stream no longer starts only once the slice is in LDS. (Activation loads
+  // issued after the prologue would wait for the weights as well; slices of
+  // more than XPRE pieces per thread stage their remainder that way.)
   // Workgroups of one rank that share an XCD stage the same slice at the same
   // time; each starts at a different point of it (a rotation of the piece
   // order) so that their requests for the same lines do not queue on one L2
   // channel together.
   // Pieces are 16-byte chunks, K fastest (piece q: token q / kp, chunk
   // q % kp), so every 4-lane group of a load reads one contiguous run.
+  // Loads per thread issued ahead of the weights: with 512 lanes 128 KiB
+  // (two token tiles), 64 KiB (one, one workgroup per CU), or 32 KiB where
+  // two workgroups share a CU's registers.
+  constexpr int XPRE = NT > 1 ? 16 : (STORER ? 8 : 4);
   const int kp = p.ks / 8;  // chunks per token
   const int pieces = T * kp;
   const int rot = (int)(((unsigned)gi % 32u) * (unsigned)(pieces / 32));
@@ -516,9 +525,9 @@ void splitk_stream_kernel(GemmParams p) {
     const int q = pc + rot;
     return q >= pieces ? q - pieces : q;
   };
-  auto stage_load = [&](int p0, u32x4 (&v)[XBATCH]) {
+  auto stage_load = [&]<int NB>(int p0, u32x4 (&v)[NB]) {
 #pragma unroll
-    for (int b = 0; b < XBATCH; ++b) {
+    for (int b = 0; b < NB; ++b) {
       const int pc = p0 + b * THREADS;
       const int q = piece(pc);
       const int t = q / kp;
@@ -526,9 +535,9 @@ void splitk_stream_kernel(GemmParams p) {
       v[b] = ld16_if(pc < pieces, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(kbase + k)) * 2u);
     }
   };
-  auto stage_store = [&](int p0, const u32x4 (&v)[XBATCH]) {
+  auto stage_store = [&]<int NB>(int p0, const u32x4 (&v)[NB]) {
 #pragma unroll
-    for (int b = 0; b < XBATCH; ++b) {
+    for (int b = 0; b < NB; ++b) {
       const int pc = p0 + b * THREADS;
       if (pc < pieces) {
         const int q = piece(pc);
@@ -544,17 +553,28 @@ void splitk_stream_kernel(GemmParams p) {
       }
     }
   };
+  // With one token tile (T <= 16) the slice is small and staging short: the
+  // prologue then goes out after the barrier as before (measured: issuing it
+  // first gained 1-1.6 us at T=24/32 K=N=16384, and lost 0.9 us at T=1).
+  constexpr bool EARLY = NT > 1;
   {
-    u32x4 v[XBATCH];
+    u32x4 v[XPRE];
     stage_load(tid, v);
+    __builtin_amdgcn_sched_barrier(0);  // the activation loads stay ahead of the weights
+    if (EARLY && !epi_wave) {
+#pragma unroll
+      for (int s = 0; s < DR; ++s) issue(s);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     stage_store(tid, v);
-    for (int p0 = tid + THREADS * XBATCH; p0 < pieces; p0 += THREADS * XBATCH) {
-      stage_load(p0, v);
-      stage_store(p0, v);
+    for (int p0 = tid + THREADS * XPRE; p0 < pieces; p0 += THREADS * XBATCH) {
+      u32x4 w[XBATCH];
+      stage_load(p0, w);
+      stage_store(p0, w);
     }
   }
   __syncthreads();
-  if (!epi_wave) {
+  if (!EARLY && !epi_wave) {
 #pragma unroll
     for (int s = 0; s < DR; ++s) issue(s);
   }
@@ -573,8 +593,8 @@ void splitk_stream_kernel(GemmParams p) {
 
   // C / partial offsets of this lane's quad (token tt*16 + li, features
   // tile*16 + 4g .. +3).
-  auto c_off = [&](int tile, int tt) -> uint32_t {
-    return ((uint32_t)(tt * 16 + li) * (uint32_t)N + (uint32_t)(tile * 16 + 4 * g)) * 2u;
+  auto c_el = [&](int tile, int tt) -> uint32_t {
+    return (uint32_t)(tt * 16 + li) * (uint32_t)N + (uint32_t)(tile * 16 + 4 * g);
   };
   auto p_off = [&](int r, int tile, int tt) -> uint32_t {
     return (((uint32_t)r * (uint32_t)T + (uint32_t)(tt * 16 + li)) * (uint32_t)N +
@@ -599,7 +619,7 @@ void splitk_stream_kernel(GemmParams p) {
 #pragma unroll
             for (int r = 1; r < 8; ++r)
               if (r < S) tot += ld[tt][r];
-            st8_if(in_t(tt), bf16_quad(tot), cr, c_off(ld_tile, tt));
+            store_quad(co, in_t(tt), tot, c_el(ld_tile, tt));
           }
           ld_tile = -1;
         }
@@ -640,7 +660,7 @@ void splitk_stream_kernel(GemmParams p) {
           for (int tt = 0; tt < NT; ++tt) acc[tt] += red[(w * NT + tt) * 64 + lane];
         if (S == 1) {
 #pragma unroll
-          for (int tt = 0; tt < NT; ++tt) st8_if(in_t(tt), bf16_quad(acc[tt]), cr, c_off(tile, tt));
+          for (int tt = 0; tt < NT; ++tt) store_quad(co, in_t(tt), acc[tt], c_el(tile, tt));
           continue;
         }
         finish_stage();
@@ -724,7 +744,7 @@ void splitk_stream_kernel(GemmParams p) {
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt) {
         if (S == 1)
-          st8_if(in_t(tt), bf16_quad(acc[tt]), cr, c_off(tile, tt));
+          store_quad(co, in_t(tt), acc[tt], c_el(tile, tt));
         else if (p.pdefer)
           pbuf[(k * NT + tt) * 64 + lane] = acc[tt];
         else
@@ -808,7 +828,7 @@ void splitk_stream_kernel(GemmParams p) {
 #pragma unroll
           for (int tt = 0; tt < NT; ++tt) {
             if (S == 1)
-              st8_if(in_t(tt), bf16_quad(sum[tt]), cr, c_off(tile, tt));
+              store_quad(co, in_t(tt), sum[tt], c_el(tile, tt));
             else
               pbuf[(k * NT + tt) * 64 + lane] = sum[tt];
           }
@@ -898,8 +918,8 @@ void splitk_stream_kernel(GemmParams p) {
           s1 += v1[r];
         }
       }
-      st8_if(ok, bf16_quad(s0), cr, c_off(t0, tt));
-      st8_if(ok1, bf16_quad(s1), cr, c_off(t1c, tt));
+      store_quad(co, ok, s0, c_el(t0, tt));
+      store_quad(co, ok1, s1, c_el(t1c, tt));
     }
   };
   // Finishes the tiles of the lanes set in `mask` (list position of lane b:

@@ -31,6 +31,10 @@ struct GemmParams {
   uint64_t bw, bws, bx, bc;  // bytes between problems: W (or Wq), Wscale, X, C
   uint64_t bpart;            // floats between problems' partials
   uint32_t bcnt;             // counters between problems' counters
+  // Output format: 0 bf16 C [T, N]; 1 E4M3FN bytes C [T, N] holding
+  // sum * c_scale saturated to +-448 (device/out.h).
+  int out_e4m3;
+  float c_scale;
 };
 
 // Choices the library normally makes itself, which tests and tuning runs can

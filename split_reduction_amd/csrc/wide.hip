@@ -28,6 +28,7 @@
 //    last rank to arrive finishes the column instead.
 
 #include "device/mfma.h"
+#include "device/out.h"
 #include "device/pack.h"
 #include "device/types.h"
 #include "device/wfmt.h"
@@ -240,16 +241,16 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
 
   // ---- output ------------------------------------------------------------------
   const int n_lane = n0 + wn * RG * 16 + 4 * g;  // feature of quad element 0, rg = 0
-  const rsrc_t cr = make_rsrc(p.c, (uint32_t)T * (uint32_t)N * 2u);
-  auto c_off = [&](int rg, int tt) -> uint32_t {
-    return ((uint32_t)(tt * 16 + li) * (uint32_t)N + (uint32_t)(n_lane + rg * 16)) * 2u;
+  const COut co = make_cout(p);
+  auto c_el = [&](int rg, int tt) -> uint32_t {
+    return (uint32_t)(tt * 16 + li) * (uint32_t)N + (uint32_t)(n_lane + rg * 16);
   };
   auto in_t = [&](int tt) -> bool { return tt * 16 + li < T; };
   if (S == 1) {
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) st8_if(in_t(tt), bf16_quad(acc[rg][tt]), cr, c_off(rg, tt));
+      for (int tt = 0; tt < NT; ++tt) store_quad(co, in_t(tt), acc[rg][tt], c_el(rg, tt));
     stamp[3] = stamp[2];
     write_stamps();
     return;
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
           f32x4 tot = part_of(0);
 #pragma unroll
           for (int r = 1; r <= OTHERS; ++r) tot += part_of(r);
-          st8_if(in_t(tt), bf16_quad(tot), cr, c_off(rg, tt));
+          store_quad(co, in_t(tt), tot, c_el(rg, tt));
         }
       }
     }

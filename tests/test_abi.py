@@ -284,3 +284,14 @@ def test_override_pins_and_restores():
     assert lib.skgemm_set_override(99, 0) == sk.SKGEMM_EINVAL
     assert lib.skgemm_set_override(-1, 0) == sk.SKGEMM_EINVAL
     assert lib.skgemm_set_override(0, -2) == sk.SKGEMM_EINVAL
+
+
+def test_e4m3_output_scale_checked_before_device_work():
+    _ensure_built()
+    lib = sk.lib()
+    a = 1 << 20
+    f = ctypes.c_float
+    for bad in (0.0, -2.0, float("nan"), float("inf")):
+        assert lib.skgemm_bf16_e4m3(a, a, a, f(bad), 1, 16, 64, 1, None) == sk.SKGEMM_EINVAL
+    assert lib.skgemm_bf16_e4m3(a, a, a, f(1.0), 1, 24, 64, 1, None) == sk.SKGEMM_ESHAPE
+    assert lib.skgemm_bf16_e4m3(None, None, None, f(1.0), 0, 16, 64, 1, None) == sk.SKGEMM_OK

@@ -288,3 +288,45 @@ def test_mxfp8_planted_mistakes_fail():
     e5m2 = np.array([[(-1.0) ** (int(c) >> 7) * (1 + (int(c) & 3) / 4) * 2.0 ** (((int(c) >> 2) & 31) - 15) for c in row]
                      for row in wq8])
     assert not np.allclose(good[:, :32], e5m2[:, :32])
+
+
+# ------------------------------------------------ E4M3 output (saturated) ---
+
+
+def test_e4m3_rne_sat_agrees_in_range():
+    """In range, the float64 output rounding is the packing helper's rounding
+    (pinned to torch above) on every probe value."""
+    v = _e4m3_probe_values()
+    assert np.array_equal(F.e4m3_rne_sat(v.astype(np.float64)), F.f32_to_e4m3_rne(v))
+    for val, code, *_ in golden_rows("e4m3_cases.txt"):
+        assert int(F.e4m3_rne_sat(np.float64([float(val)]))[0]) == int(code, 16), val
+
+
+def test_e4m3_rne_sat_saturates_and_rounds_in_float64():
+    # saturation: anything beyond 448 in magnitude is +-448 (0x7E / 0xFE)
+    big = np.array([448.0, 448.0000001, 464.0, 500.0, 1e30, -449.0, -1e300])
+    assert list(F.e4m3_rne_sat(big)) == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    # midpoints decided by float64 values that float32 cannot hold:
+    # 17 is the tie of 16 (0x58, even) and 18 (0x59); 19 the tie of 18 and 20 (0x5A)
+    eps = 1e-12
+    cases = {17.0: 0x58, 17.0 + eps: 0x59, 17.0 - eps: 0x58, 19.0: 0x5A, 19.0 - eps: 0x59,
+             25.0: 0x5C, 25.0 + eps: 0x5D, -17.0: 0xD8, 0.0009765625 + eps: 0x01}
+    for x, code in cases.items():
+        assert int(F.e4m3_rne_sat(np.float64([x]))[0]) == code, (x, code)
+
+
+def test_e4m3_rne_sat_planted_mistakes_fail():
+    """Truncation instead of nearest, or no saturation, would fail the pins."""
+    mags = F.e4m3_value(np.arange(0x7F))
+
+    def truncating(x):
+        a = np.clip(np.abs(x), 0, 448)
+        c = np.searchsorted(mags, a, side="right") - 1
+        return (c | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+    x = np.float64([17.0 + 1e-12, 19.0])
+    assert not np.array_equal(truncating(x), F.e4m3_rne_sat(x))
+    with pytest.raises(ValueError):
+        F.f32_to_e4m3_rne(np.float32([500.0]))  # the unsaturated rounding rejects it
+    with pytest.raises(ValueError):
+        F.e4m3_rne_sat(np.float64([np.nan]))

@@ -144,3 +144,29 @@ def test_mxfp8_gemm_matches_bruteforce_and_integer_exact():
     bf = G.gemm_bruteforce(F.bf16_bits_to_f64(x).tolist(), wv.tolist())
     assert np.array_equal(got, np.array(bf))
     assert np.array_equal(got, np.round(got))
+
+
+def test_e4m3_output_reference_and_bound():
+    """The E4M3-output GEMM reference: integer operands give exact sums, so
+    with a power-of-two scale the codes are the rounding of exact values
+    (checked against the brute force), saturation caps them at +-448, and the
+    acceptance bound passes the exact codes and fails codes one step off."""
+    rng = np.random.default_rng(11)
+    T, N, K = 3, 8, 96
+    x = rng.integers(-3, 4, size=(T, K)).astype(np.float32)
+    w = rng.integers(-3, 4, size=(N, K)).astype(np.float32)
+    xb, wb = workloads.to_bf16_bits(x), workloads.to_bf16_bits(w)
+    brute = np.array(G.gemm_bruteforce(x.tolist(), w.tolist()))
+    for scale in (1.0, 0.25, 8.0):
+        y, codes = G.gemm_bf16_e4m3_ref(xb, wb, scale)
+        assert np.array_equal(y, np.clip(brute * scale, -448, 448))
+        assert np.array_equal(codes, F.e4m3_rne_sat(np.clip(brute * scale, -448, 448)))
+        assert G.e4m3_out_violation_ratio(codes, brute, K, scale) <= 1.0
+    y, codes = G.gemm_bf16_e4m3_ref(xb, wb, 8.0)
+    assert np.all(np.abs(F.e4m3_value(codes)) <= 448) and np.any(np.abs(brute * 8.0) > 448)
+    # a code one step away from a large value breaks the bound
+    big = np.array([[300.0]])
+    good = F.e4m3_rne_sat(big)
+    off = (good.astype(np.int64) + 2).astype(np.uint8)  # two E4M3 steps up: 352 instead of 288/320
+    assert G.e4m3_out_violation_ratio(good, big, 1, 1.0) <= 1.0
+    assert G.e4m3_out_violation_ratio(off, big, 1, 1.0) > 1.0
