@@ -311,6 +311,99 @@ def run_workload(wl, steps, warmup, host_w=None) -> dict:
 
 
 # ---------------------------------------------------------------------------
+# Chained launches (the pages' launch overlap)
+# ---------------------------------------------------------------------------
+
+CHAIN_DIMS = [7168, 2048] * 4 + [7168]  # eight steps: the T=8 K=7168 N=2048 shape and its transpose
+
+
+def chain_bench(steps: int, warmup: int, T: int = 8, S: int = 4) -> dict:
+    """Per-step time of eight dependent GEMMs (X of step i+1 is C of step i),
+    alternating K=7168 -> N=2048 and K=2048 -> N=7168 (29.4 MB of bf16 weights
+    each), T=8, split_k=4, cold weights (sets of the eight matrices rotated
+    through >= 1 GiB): one skgemm_bf16_chain launch per chain, against the
+    same eight steps as separate skgemm_bf16 launches replayed from a graph."""
+    import torch
+
+    import split_reduction_amd as sk
+
+    dev = "cuda:0"
+    L = len(CHAIN_DIMS) - 1
+    rng = np.random.default_rng(SEED_CHAIN)
+    base = [torch.from_numpy(workloads.normal_bf16(rng, (CHAIN_DIMS[i + 1], CHAIN_DIMS[i]), 0.02).view(np.int16))
+            .to(dev).view(torch.bfloat16) for i in range(L)]
+    set_bytes = sum(w.numel() * 2 for w in base)
+    R = max(2, math.ceil(ROTATE_BYTES / set_bytes))
+    sets = [base] + [[w.clone() for w in base] for _ in range(R - 1)]
+    X = torch.from_numpy(workloads.normal_bf16(rng, (T, CHAIN_DIMS[0]), 1.0).view(np.int16)).to(dev).view(torch.bfloat16)
+    Cs = [torch.empty((T, d), dtype=torch.bfloat16, device=dev) for d in CHAIN_DIMS[1:]]
+    stream = torch.cuda.Stream()
+    sk.skgemm_reserve(T, max(CHAIN_DIMS), S, stream)
+
+    def chain(i):
+        sk.skgemm_bf16_chain(sets[i % R], X, Cs, CHAIN_DIMS, T, S, stream)
+
+    def separate(i):
+        ws = sets[i % R]
+        for j in range(L):
+            sk.skgemm_bf16(ws[j], X if j == 0 else Cs[j - 1], Cs[j], T, CHAIN_DIMS[j + 1], CHAIN_DIMS[j], S, stream)
+
+    def timed(fn, n, graph):
+        with torch.cuda.stream(stream):
+            for i in range(warmup):
+                fn(i)
+        stream.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for i in range(n):
+                    fn(i)
+            with torch.cuda.stream(stream):
+                g.replay()
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                start.record(stream)
+                g.replay()
+                end.record(stream)
+        else:
+            with torch.cuda.stream(stream):
+                start.record(stream)
+                for i in range(n):
+                    fn(i)
+                end.record(stream)
+        end.synchronize()
+        return start.elapsed_time(end) * 1e3 / (n * L)
+
+    # a longer chain of the same steps: the launch's fixed cost spread wider
+    L4 = 4 * L
+    dims4 = CHAIN_DIMS + CHAIN_DIMS[1:] * 3
+    Cs4 = [torch.empty((T, d), dtype=torch.bfloat16, device=dev) for d in dims4[1:]]
+
+    def chain4(i):
+        ws = sets[i % R] * 4
+        sk.skgemm_bf16_chain(ws, X, Cs4, dims4, T, S, stream)
+
+    n = max(10, steps // 4)
+    t_chain = timed(chain, n, graph=False)
+    t_chain4 = timed(chain4, max(4, n // 4), graph=False) * L / L4
+    t_sep = timed(separate, n, graph=True)
+    del sets, base
+    torch.cuda.empty_cache()
+    return {"steps": L, "T": T, "split_k": S, "dims": CHAIN_DIMS,
+            "weight_bytes_per_step": set_bytes // L, "chains_timed": n,
+            "t_us_per_step_chain_launch": round(t_chain, 3),
+            "t_us_per_step_chain_launch_32_steps": round(t_chain4, 3),
+            "t_us_per_step_separate_launches_graph": round(t_sep, 3),
+            "weight_TBps_chain": round(set_bytes / L / (t_chain * 1e-6) / 1e12, 4),
+            "timing": "chain: eager launches on one stream, HIP events; separate: one graph of all launches"}
+
+
+SEED_CHAIN = workloads.SEED_BASE + 300
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on the host cores
 # ---------------------------------------------------------------------------
 
@@ -665,6 +758,12 @@ def main() -> None:
             log(json.dumps(r))
             extra.append(r)
 
+    chain = None
+    if not args.only_headline:
+        log("chained launches")
+        chain = chain_bench(args.steps, max(3, args.warmup // 2))
+        log(json.dumps(chain))
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -699,6 +798,7 @@ def main() -> None:
         "read_probe": h["read_probe"],
         "tactic": h["tactic"],
         "workloads": extra,
+        "chain": chain,
         "kernel_source_sha": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

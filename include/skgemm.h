@@ -104,6 +104,36 @@ SKGEMM_API int skgemm_bf16_e4m3(const void* W, const void* X, void* C8, float c_
                                 int K, int split_k, hipStream_t stream);
 
 /*
+ * skgemm_bf16_chain: L dependent GEMMs in one launch, the output of each the
+ * activations of the next: step i computes C[i][T, dims[i+1]] =
+ * A_i . W[i]^T with A_0 = X and A_i = C[i-1], each step as skgemm_bf16 would
+ * (split_k contiguous K slices in FP32, rank-order sum, bf16 RNE, stored
+ * once). This is the launch overlap of page
+ * vllm.models.kimi_k3.nvidia.specialized_decode.cutedsl.gemm.splitk
+ * (SplitKGemm.__call__ with use_pdl: the weight loads of the next kernel go
+ * out before it waits for its predecessor, the activation loads after): the
+ * weights of step i+1 are loaded while step i finishes, and only the
+ * activation loads wait for C[i] (a grid-wide barrier between steps).
+ *   W, C     host arrays of L device pointers: W[i] bf16 [dims[i+1], dims[i]],
+ *            C[i] bf16 [T, dims[i+1]], 16-byte aligned; C[i] must not
+ *            overlap its input (X for i = 0, else C[i-1]) (SKGEMM_EINVAL).
+ *   X        bf16 [T, dims[0]], device memory, 16-byte aligned.
+ *   dims     host array of L + 1 sizes, each >= 1 and within the size limits.
+ *   1 <= L <= SKGEMM_MAX_CHAIN, 1 <= T <= 16, split_k in {1, 2, 4, 8}.
+ *   Shapes: dims[i] % (32 * split_k) == 0 for i < L and dims[i] % 16 == 0
+ *   for i >= 1 (SKGEMM_ESHAPE).
+ * The launch is cooperative (all workgroups resident at once, one per CU);
+ * it uses the stream's workspace for its barrier words, so chains on one
+ * stream are ordered and chains on different streams do not share them. A
+ * barrier wait that runs out (not expected: the launch is cooperative) is
+ * recorded in skgemm_health as a record with tile group 0xFFFFFFFF and the
+ * step as its rank.
+ */
+#define SKGEMM_MAX_CHAIN 64
+SKGEMM_API int skgemm_bf16_chain(const void* const* W, const void* X, void* const* C, const int* dims,
+                                 int L, int T, int split_k, hipStream_t stream);
+
+/*
  * skgemm_bf16_noalloc: skgemm_bf16 for callers that cannot allocate device
  * memory -- code under HIP graph capture without a prior skgemm_reserve,
  * tight serving loops, harnesses that forbid hipMalloc. Same arguments,

@@ -116,6 +116,37 @@ def violation_ratio(c_test: np.ndarray, c_ref: np.ndarray, k: int, rms=None) -> 
 
 
 # ---------------------------------------------------------------------------
+# Chained GEMMs
+# ---------------------------------------------------------------------------
+
+
+def gemm_chain_ref(x_bits: np.ndarray, w_bits_list) -> list:
+    """The outputs C_0 .. C_(L-1) of a chain C_i = bf16(A_i . W_i^T) with
+    A_0 = X and A_i = C_(i-1) (the pages' dependent launches: each step's
+    activations are the previous step's stored bf16 output), as float64
+    values of the bf16 outputs.
+
+    Defined here for chains whose every output is exactly representable in
+    bf16 (checked; a ValueError otherwise): the bf16 rounding between steps is
+    then the identity and the chain is exact. Chains of general values are
+    checked step by step instead, each step on the stored output of the one
+    before it (gemm_bf16_ref)."""
+    from .formats import f32_to_bf16_rne
+
+    a_bits = np.asarray(x_bits, dtype=np.uint16)
+    outs = []
+    for w_bits in w_bits_list:
+        c = gemm_bf16_ref(a_bits, w_bits)
+        c32 = c.astype(np.float32)
+        bits = f32_to_bf16_rne(c32)
+        if not np.array_equal(bf16_bits_to_f64(bits), c):
+            raise ValueError("a chain output is not exactly representable in bf16")
+        outs.append(c)
+        a_bits = bits
+    return outs
+
+
+# ---------------------------------------------------------------------------
 # E4M3 output
 # ---------------------------------------------------------------------------
 

@@ -65,6 +65,7 @@ def _declare(lib):
         "skgemm_set_override": [i, i],
         "skgemm_bf16_noalloc": [vp, vp, vp, i, i, i, i, st],
         "skgemm_bf16_e4m3": [vp, vp, vp, ctypes.c_float, i, i, i, i, st],
+        "skgemm_bf16_chain": [vp, vp, vp, vp, i, i, i, st],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -171,6 +172,20 @@ def skgemm_bf16_e4m3(W, X, C8, c_scale: float, T: int, N: int, K: int, split_k: 
     code = lib().skgemm_bf16_e4m3(_ptr(W, 2 * _n(N, K), "W"), _ptr(X, 2 * _n(T, K), "X"),
                                   _ptr(C8, _n(T, N), "C8"), float(c_scale), T, N, K, split_k, _stream(stream))
     _check(code, "skgemm_bf16_e4m3")
+
+
+def skgemm_bf16_chain(Ws, X, Cs, dims, T: int, split_k: int, stream=None) -> None:
+    """L GEMMs in one launch, C[i] = A_i . W[i]^T with A_0 = X, A_i = C[i-1];
+    Ws and Cs are sequences of L tensors (or addresses), dims L + 1 sizes."""
+    L = len(Ws)
+    if len(Cs) != L or len(dims) != L + 1:
+        raise SkgemmError(SKGEMM_EINVAL, "skgemm_bf16_chain: need L weights, L outputs and L + 1 dims")
+    wp = (ctypes.c_void_p * max(L, 1))(*[_ptr(Ws[i], 2 * _n(dims[i + 1], dims[i]), f"W[{i}]") for i in range(L)])
+    cp = (ctypes.c_void_p * max(L, 1))(*[_ptr(Cs[i], 2 * _n(T, dims[i + 1]), f"C[{i}]") for i in range(L)])
+    dp = (ctypes.c_int * (L + 1))(*[int(d) for d in dims])
+    code = lib().skgemm_bf16_chain(wp, _ptr(X, 2 * _n(T, dims[0]) if dims else 0, "X"), cp, dp, L, T, split_k,
+                                   _stream(stream))
+    _check(code, "skgemm_bf16_chain")
 
 
 def skgemm_bf16_noalloc(W, X, C, T: int, N: int, K: int, split_k: int, stream=None) -> None:

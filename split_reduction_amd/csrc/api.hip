@@ -92,7 +92,9 @@ int ensure_workspace(hipStream_t stream, size_t part_bytes, size_t cnt_count, Wo
   if (e != hipSuccess) return hip_fail(e);
   std::lock_guard<std::mutex> lock(g_ws_mu);
   Workspace& w = g_ws[std::make_pair(dev, stream)];
-  if (w.part_bytes >= part_bytes && w.cnt_count >= cnt_count) {
+  // A new entry holds nothing yet (a call asking for no bytes still needs the
+  // counter, health and synchronisation words).
+  if (w.cnt != nullptr && w.part_bytes >= part_bytes && w.cnt_count >= cnt_count) {
     *out = w;
     return SKGEMM_OK;
   }
@@ -104,7 +106,7 @@ int ensure_workspace(hipStream_t stream, size_t part_bytes, size_t cnt_count, Wo
   nw.part_bytes = std::max(part_bytes, (size_t)256);
   nw.cnt_count = std::max(cnt_count, (size_t)64);
   if (hipMalloc((void**)&nw.part, nw.part_bytes) != hipSuccess) return SKGEMM_ENOMEM;
-  const size_t words = nw.cnt_count + skg::kHealthWords;
+  const size_t words = nw.cnt_count + skg::kHealthWords + skg::kSyncWords;
   if (hipMalloc((void**)&nw.cnt, words * sizeof(uint32_t)) != hipSuccess) {
     (void)hipFree(nw.part);
     return SKGEMM_ENOMEM;
@@ -309,6 +311,52 @@ SKGEMM_API int skgemm_bf16_e4m3(const void* W, const void* X, void* C8, float c_
   out.e4m3 = 1;
   out.c_scale = c_scale;
   return run_gemm(skg::kBf16, W, nullptr, X, C8, T, N, K, split_k, stream, Batch{}, nullptr, out);
+}
+
+SKGEMM_API int skgemm_bf16_chain(const void* const* W, const void* X, void* const* C, const int* dims,
+                                 int L, int T, int split_k, hipStream_t stream) {
+  if (W == nullptr || C == nullptr || dims == nullptr || X == nullptr) return SKGEMM_EINVAL;
+  if (L < 1 || L > SKGEMM_MAX_CHAIN || T < 1 || T > 16) return SKGEMM_EINVAL;
+  if (split_k != 1 && split_k != 2 && split_k != 4 && split_k != 8) return SKGEMM_EINVAL;
+  for (int i = 0; i <= L; ++i) {
+    if (dims[i] < 1) return SKGEMM_EINVAL;
+    if (dims[i] > SKGEMM_MAX_K || dims[i] > SKGEMM_MAX_N) return SKGEMM_ESHAPE;
+  }
+  if (!aligned16(X)) return SKGEMM_EALIGN;
+  const int cus = device_cus();
+  skg::ChainParams p{};
+  for (int i = 0; i < L; ++i) {
+    if (W[i] == nullptr || C[i] == nullptr) return SKGEMM_EINVAL;
+    if (!aligned16(W[i]) || !aligned16(C[i])) return SKGEMM_EALIGN;
+    if (dims[i] % (32 * split_k) != 0 || dims[i + 1] % 16 != 0) return SKGEMM_ESHAPE;
+    // K folded two ways (8-row tiles) where 16-row tiles would leave CUs
+    // idle and the tokens fit in half an MFMA operand.
+    p.fold[i] = (T <= 8 && dims[i + 1] / 16 < (cus > 0 ? cus : 256) && dims[i] % (64 * split_k) == 0) ? 2 : 1;
+    // C[i] must not overlap the activations it is computed from.
+    const uintptr_t a0 = (uintptr_t)(i == 0 ? X : C[i - 1]);
+    const uintptr_t a1 = a0 + (uintptr_t)T * (uintptr_t)dims[i] * 2;
+    const uintptr_t c0 = (uintptr_t)C[i], c1 = c0 + (uintptr_t)T * (uintptr_t)dims[i + 1] * 2;
+    if (c0 < a1 && a0 < c1) return SKGEMM_EINVAL;
+  }
+  Workspace wsp;
+  int rc = ensure_workspace(stream, 0, 0, &wsp);
+  if (rc != SKGEMM_OK) return rc;
+  if (wsp.cnt == nullptr) return SKGEMM_ENOMEM;  // the barrier words must exist
+  for (int i = 0; i < L; ++i) {
+    p.w[i] = W[i];
+    p.c[i] = C[i];
+  }
+  for (int i = 0; i <= L; ++i) p.dims[i] = dims[i];
+  p.x = X;
+  p.L = L;
+  p.T = T;
+  p.S = split_k;
+  p.health = wsp.cnt + wsp.cnt_count;
+  p.sync = p.health + skg::kHealthWords;
+  p.wait_ticks = 20000000u;  // 200 ms: a barrier wait that long means something is broken
+  if (cus <= 0) return hip_fail(hipErrorInvalidDevice);
+  const hipError_t e = skg::launch_chain(p, cus, stream);
+  return e == hipSuccess ? SKGEMM_OK : hip_fail(e);
 }
 
 SKGEMM_API int skgemm_bf16_noalloc(const void* W, const void* X, void* C, int T, int N, int K,

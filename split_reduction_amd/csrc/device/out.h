@@ -34,23 +34,27 @@ __device__ __forceinline__ float e4m3_in_range(float x, float scale) {
 }
 
 // Four consecutive outputs of one token, element index `el` (el % 4 == 0).
+// POL: the stores' cache policy (device-coherent where another CU reads C
+// within the same launch).
+template <int POL = kPolicyDefault>
 __device__ __forceinline__ void store_quad(const COut& o, bool ok, f32x4 v, uint32_t el) {
   if (o.e4m3) {
     const uint32_t w = e4m3_pack4(e4m3_in_range(v.x, o.scale), e4m3_in_range(v.y, o.scale),
                                   e4m3_in_range(v.z, o.scale), e4m3_in_range(v.w, o.scale));
-    st4_if(ok, w, o.r, el);
+    __builtin_amdgcn_raw_buffer_store_b32(w, o.r, ok ? el : kOOB, 0, POL);
   } else {
-    st8_if(ok, bf16_quad(v), o.r, el * 2u);
+    __builtin_amdgcn_raw_buffer_store_b64(bf16_quad(v), o.r, ok ? el * 2u : kOOB, 0, POL);
   }
 }
 
 // Two consecutive outputs of one token, element index `el` (el % 2 == 0).
+template <int POL = kPolicyDefault>
 __device__ __forceinline__ void store_pair(const COut& o, bool ok, float a, float b, uint32_t el) {
   if (o.e4m3) {
     const int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_in_range(a, o.scale), e4m3_in_range(b, o.scale), 0, false);
-    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w & 0xFFFF), o.r, ok ? el : kOOB, 0, kPolicyDefault);
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(w & 0xFFFF), o.r, ok ? el : kOOB, 0, POL);
   } else {
-    st4_if(ok, bf16_pair(a, b), o.r, el * 2u);
+    __builtin_amdgcn_raw_buffer_store_b32(bf16_pair(a, b), o.r, ok ? el * 2u : kOOB, 0, POL);
   }
 }
 

@@ -66,6 +66,10 @@ constexpr int kCntStride = 32;
 // owner rank, problem, ticks waited}.
 constexpr int kHealthRecords = 15;
 constexpr int kHealthWords = 8 + 8 * kHealthRecords;
+// Synchronisation words after the health words of a workspace (the chain
+// kernel's grid barrier: a generation, a global count and eight group
+// counts, one 128-byte line each).
+constexpr int kSyncWords = 10 * kCntStride;
 
 // Records one owner time-out (vector atomics and stores only).
 __device__ __forceinline__ void note_timeout(uint32_t* health, uint32_t group, uint32_t rank,
@@ -144,6 +148,24 @@ hipError_t launch_wide(const Tactic& t, const GemmParams& p, hipStream_t stream)
 
 // Enqueues one launch (T <= 128). Returns the launch's hipError_t.
 hipError_t launch_gemm(const Tactic& tac, const GemmParams& p, hipStream_t stream);
+
+// A chain of GEMMs in one cooperative launch (chain.hip): step i multiplies
+// A_i [T, dims[i]] (A_0 = x, A_i = c[i-1]) by w[i] [dims[i+1], dims[i]]^T
+// into c[i] [T, dims[i+1]], all bf16, split_k = S for every step.
+constexpr int kMaxChain = 64;  // SKGEMM_MAX_CHAIN
+struct ChainParams {
+  const void* w[kMaxChain];
+  void* c[kMaxChain];
+  const void* x;
+  int dims[kMaxChain + 1];
+  int fold[kMaxChain];  // per step: K folded 1 or 2 ways (16 / fold rows per tile)
+  int L, T, S;
+  uint32_t* sync;    // grid barrier words (kSyncWords, one 128-byte line each):
+                     // generation, global count, 8 group counts
+  uint32_t* health;  // time-out records (workspace health words)
+  uint32_t wait_ticks;
+};
+hipError_t launch_chain(const ChainParams& p, int grid, hipStream_t s);
 
 // Zeros `bytes` (a multiple of 16, 16-byte aligned) with a fill kernel.
 hipError_t launch_zero16(void* p, size_t bytes, hipStream_t s);

@@ -295,3 +295,31 @@ def test_e4m3_output_scale_checked_before_device_work():
         assert lib.skgemm_bf16_e4m3(a, a, a, f(bad), 1, 16, 64, 1, None) == sk.SKGEMM_EINVAL
     assert lib.skgemm_bf16_e4m3(a, a, a, f(1.0), 1, 24, 64, 1, None) == sk.SKGEMM_ESHAPE
     assert lib.skgemm_bf16_e4m3(None, None, None, f(1.0), 0, 16, 64, 1, None) == sk.SKGEMM_OK
+
+
+def test_chain_arguments_checked_before_device_work():
+    _ensure_built()
+    lib = sk.lib()
+    a = 1 << 20
+    P = ctypes.c_void_p
+
+    def arrs(L, dims, cbase=1 << 30):
+        w = (P * L)(*([a] * L))
+        c = (P * L)(*[cbase + (i << 24) for i in range(L)])
+        d = (ctypes.c_int * (L + 1))(*dims)
+        return w, c, d
+
+    w, c, d = arrs(2, [7168, 2048, 7168])
+    assert lib.skgemm_bf16_chain(w, a, c, d, 0, 8, 4, None) == sk.SKGEMM_EINVAL    # L = 0
+    assert lib.skgemm_bf16_chain(w, a, c, d, 2, 17, 4, None) == sk.SKGEMM_EINVAL   # T > 16
+    assert lib.skgemm_bf16_chain(w, a, c, d, 2, 8, 3, None) == sk.SKGEMM_EINVAL    # split_k
+    assert lib.skgemm_bf16_chain(None, a, c, d, 2, 8, 4, None) == sk.SKGEMM_EINVAL
+    assert lib.skgemm_bf16_chain(w, a + 8, c, d, 2, 8, 4, None) == sk.SKGEMM_EALIGN
+    w, c, d = arrs(2, [7168, 2040, 7168])
+    assert lib.skgemm_bf16_chain(w, a, c, d, 2, 8, 4, None) == sk.SKGEMM_ESHAPE    # N % 16
+    w, c, d = arrs(1, [1088, 2048])
+    assert lib.skgemm_bf16_chain(w, a, c, d, 1, 8, 4, None) == sk.SKGEMM_ESHAPE    # K % (64 * 4) at T <= 8
+    w, c, d = arrs(1, [1024, 2048], cbase=a)  # C[0] on top of X
+    assert lib.skgemm_bf16_chain(w, a, c, d, 1, 8, 4, None) == sk.SKGEMM_EINVAL
+    w, c, d = arrs(65, [1024] * 66)
+    assert lib.skgemm_bf16_chain(w, a, c, d, 65, 8, 4, None) == sk.SKGEMM_EINVAL   # L > 64

@@ -9,6 +9,7 @@ fixed-order butterfly against hand-derived values.
 import math
 
 import numpy as np
+import pytest
 
 from oracle import formats as F
 from oracle import gemm as G
@@ -170,3 +171,28 @@ def test_e4m3_output_reference_and_bound():
     off = (good.astype(np.int64) + 2).astype(np.uint8)  # two E4M3 steps up: 352 instead of 288/320
     assert G.e4m3_out_violation_ratio(good, big, 1, 1.0) <= 1.0
     assert G.e4m3_out_violation_ratio(off, big, 1, 1.0) > 1.0
+
+
+def test_chain_reference_is_the_composed_product():
+    """Signed two-term selections keep every chain value a small integer, so
+    the chain's outputs are exactly the composition of the plain products
+    (brute force, step by step), and a value that bf16 cannot hold is refused."""
+    rng = np.random.default_rng(12)
+    T, dims = 3, [64, 32, 96, 64]
+    x = rng.integers(-1, 2, size=(T, dims[0])).astype(np.float32)
+    ws = []
+    for i in range(len(dims) - 1):
+        w = np.zeros((dims[i + 1], dims[i]), dtype=np.float32)
+        for n in range(dims[i + 1]):
+            a, b = rng.choice(dims[i], size=2, replace=False)
+            w[n, a], w[n, b] = rng.choice([-1.0, 1.0]), rng.choice([-1.0, 1.0])
+        ws.append(w)
+    outs = G.gemm_chain_ref(workloads.to_bf16_bits(x), [workloads.to_bf16_bits(w) for w in ws])
+    a = x.astype(np.float64)
+    for i, w in enumerate(ws):
+        a = np.array(G.gemm_bruteforce(a.tolist(), w.tolist()))
+        assert np.array_equal(outs[i], a)
+    ones_x = workloads.to_bf16_bits(np.ones((1, 257), dtype=np.float32))
+    ones_w = workloads.to_bf16_bits(np.ones((16, 257), dtype=np.float32))
+    with pytest.raises(ValueError):  # 257 needs nine significant bits
+        G.gemm_chain_ref(ones_x, [ones_w])
