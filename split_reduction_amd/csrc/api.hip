@@ -26,6 +26,11 @@ thread_local int g_last_hip_error = 0;
 // state) means the library's own choice.
 std::atomic<int> g_knobs[skg::kKnobCount];
 
+// The split-K hand-off of the persistent kernel unless a test pins one:
+// 0 arrival counter, 1 tagged mailbox.
+constexpr int kDefaultHandoff = 0;
+using skg::knob;
+
 // How long a tile's owner waits for the other split ranks before handing the
 // tile to the last to arrive: 100 us of the 100 MHz device clock unless a
 // test pins another tick count (0 exercises the hand-over path).
@@ -112,6 +117,9 @@ int ensure_workspace(hipStream_t stream, size_t part_bytes, size_t cnt_count, Wo
     return SKGEMM_ENOMEM;
   }
   e = hipMemsetAsync(nw.cnt, 0, words * sizeof(uint32_t), stream);
+  // Partials start zeroed: a mailbox tag is never 0, so no slot of a new
+  // workspace can hold a value that passes for this launch's.
+  if (e == hipSuccess) e = hipMemsetAsync(nw.part, 0, nw.part_bytes, stream);
   if (e != hipSuccess) {
     (void)hipFree(nw.part);
     (void)hipFree(nw.cnt);
@@ -178,9 +186,16 @@ int run_gemm(int wf, const void* w, const void* ws, const void* x, void* c, int 
   if (rc != SKGEMM_OK) return rc;
   if (T == 0 || N == 0) return SKGEMM_OK;
   const int L = batch.L;
+  // The tagged-mailbox hand-off (persistent kernel, single problems with a
+  // split, not in the no-allocation scratch) stores 8 bytes per partial.
+  bool mailbox = false;
+  if (S > 1 && L == 1 && given == nullptr && knob(skg::kKnobHandoff, kDefaultHandoff) == 1) {
+    skg::Tactic t0{};
+    mailbox = skg::pick_tactic(std::min(kTokenBlock, T), N, K, S, wf, &t0, L) && skg::tactic_mailbox(t0);
+  }
   Workspace wsp;
   if (S > 1) {
-    const size_t part = part_bytes_for(T, N, S) * (size_t)L, cnts = counters_for(N) * (size_t)L;
+    const size_t part = part_bytes_for(T, N, S) * (size_t)L * (mailbox ? 2 : 1), cnts = counters_for(N) * (size_t)L;
     if (given != nullptr) {
       if (part > given->part_bytes || cnts > given->cnt_count) return SKGEMM_ESCRATCH;
       wsp = *given;
@@ -218,6 +233,8 @@ int run_gemm(int wf, const void* w, const void* ws, const void* x, void* c, int 
     p.owner_wait = all_resident ? owner_wait_ticks() : 0u;
     p.pdefer = tac.pdefer;
     p.health = wsp.cnt != nullptr ? wsp.cnt + wsp.cnt_count : nullptr;
+    p.mailbox = (mailbox && skg::tactic_mailbox(tac)) ? 1 : 0;
+    p.epoch = wsp.cnt != nullptr ? p.health + skg::kHealthWords + skg::kEpochWord : nullptr;
     p.L = L;
     p.bw = batch.bw;
     p.bws = batch.bws;
@@ -522,10 +539,12 @@ SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int weight_fo
              "{\"nt\": %d, \"rg\": %d, \"wk\": %d, \"wn\": %d, \"d\": %d, \"c\": %d, \"kc\": %d, "
              "\"tile_n\": %d, \"threads\": %d, \"lds\": %d, \"grid\": %d, \"split_k\": %d, "
              "\"token_blocks\": %d, \"mxfp4\": %d, \"weight_format\": %d, \"kind\": \"%s\", "
-             "\"shape\": %d, \"fold\": %d, \"pdefer\": %d}",
+             "\"shape\": %d, \"fold\": %d, \"pdefer\": %d, \"handoff\": \"%s\"}",
              t.nt, t.rg, t.wk, t.wn, t.d, t.c, t.kc, t.tile_n, t.threads, t.lds, t.grid, split_k,
              blocks, t.wf == skg::kMxfp4 ? 1 : 0, t.wf, t.kind == 3 ? "wide" : t.kind == 2 ? "cluster" : (t.kind == 1 ? "stream" : "tiled"), t.shape,
-             t.kind == 2 ? t.fold : 1, t.pdefer);
+             t.kind == 2 ? t.fold : 1, t.pdefer,
+             split_k == 1 ? "none" : t.kind == 2 ? "lds"
+             : (knob(skg::kKnobHandoff, kDefaultHandoff) == 1 && skg::tactic_mailbox(t)) ? "mailbox" : "counter");
   }
   return SKGEMM_OK;
 }

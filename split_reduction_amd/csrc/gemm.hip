@@ -421,6 +421,7 @@ void splitk_stream_kernel(GemmParams p) {
   static_assert(!SIDE || (WK > 1 && WN == 1), "a side wave serves one column of streaming waves");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ uint32_t s_tag;  // mailbox tag of this launch
 
   uint64_t stamp[5];  // optional phase stamps (s_memrealtime, 100 MHz)
   stamp[0] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
@@ -432,6 +433,14 @@ void splitk_stream_kernel(GemmParams p) {
   const int g = lane >> 4;
   const int li = lane & 15;
   const bool epi_wave = SIDE && wave == 0;  // the side wave (epilogue or storer)
+  // Mailbox epoch (page vllm.models.muse_spark.amd.mono.kernels.dev, module
+  // note: tags are the epoch of a device word bumped once per pass, so
+  // nothing is ever zeroed): read here, before this workgroup counts itself
+  // as started; the last workgroup to start advances the word for the next
+  // launch, when every workgroup of this one has read it.
+  uint32_t epoch0 = 0;
+  if (!EPI && p.mailbox && tid == 0)
+    epoch0 = __hip_atomic_load(p.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int sw = SIDE ? wk - 1 : wk;  // index among the streaming waves of the tile
 
   const int S = p.S;
@@ -455,7 +464,9 @@ void splitk_stream_kernel(GemmParams p) {
   const rsrc_t sr = MX ? make_rsrc(p.wscale, (uint32_t)N * (uint32_t)(K / 32)) : wr;
   const rsrc_t xr = make_rsrc(p.x, (uint32_t)T * (uint32_t)K * 2u);
   const COut co = make_cout(p);
-  const rsrc_t pr = make_rsrc(p.part, (uint32_t)S * (uint32_t)T * (uint32_t)N * 4u);
+  // Partials: FP32 [S, T, N]; in the mailbox hand-off each value is an
+  // 8-byte (value, tag) pair.
+  const rsrc_t pr = make_rsrc(p.part, (uint32_t)S * (uint32_t)T * (uint32_t)N * (p.mailbox ? 8u : 4u));
   // Arrival counter of a 16-row tile: one 128-byte line each, so the S
   // ranks' arrivals and the owner's polls of one tile meet no other tile's
   // (measured: 1-3 us off the hand-off tail of T=32 K=7168 N=18432).
@@ -573,7 +584,15 @@ void splitk_stream_kernel(GemmParams p) {
       stage_store(p0, w);
     }
   }
+  if (!EPI && p.mailbox && tid == 0) s_tag = (epoch0 & 0x7FFFFFFFu) | 0x80000000u;  // never 0
   __syncthreads();
+  // This workgroup counts itself as started (after reading the epoch). The
+  // count comes back long before the workgroup ends, where the last to start
+  // advances the epoch: nothing waits for it here (256 device-scope atomics on
+  // one line are served one at a time, several microseconds in all).
+  uint32_t started_old = 0;
+  if (!EPI && p.mailbox && tid == 0)
+    started_old = __hip_atomic_fetch_add(p.epoch + kCntStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!EARLY && !epi_wave) {
 #pragma unroll
     for (int s = 0; s < DR; ++s) issue(s);
@@ -601,6 +620,28 @@ void splitk_stream_kernel(GemmParams p) {
             (uint32_t)(tile * 16 + 4 * g)) * 4u;
   };
   auto in_t = [&](int tt) -> bool { return tt * 16 + li < T; };
+
+  // Mailbox slot of this lane's quad: element (r, token, feature) is the
+  // 8-byte pair at ((r * T + token) * N + feature) * 8, the quad's four pairs
+  // in two 16-byte halves (page vllm.models.muse_spark.amd.mono.kernels.dev,
+  // mb_put2: two (value, tag) pairs per 16-byte store; mb_poll: reload until
+  // every tag matches).
+  auto m_off = [&](int r, int tile, int tt) -> uint32_t {
+    return (((uint32_t)r * (uint32_t)T + (uint32_t)(tt * 16 + li)) * (uint32_t)N +
+            (uint32_t)(tile * 16 + 4 * g)) * 8u;
+  };
+  // This rank's partial of (tile, token tile tt), device-coherent: a plain
+  // FP32 quad, or in the mailbox two tagged halves.
+  auto put_partial = [&](int tile, int tt, f32x4 v) {
+    if (p.mailbox) {
+      const uint32_t tag = s_tag;
+      const uint32_t o = m_off(rank, tile, tt);
+      st16_coherent_if(in_t(tt), u32x4{__float_as_uint(v.x), tag, __float_as_uint(v.y), tag}, pr, o);
+      st16_coherent_if(in_t(tt), u32x4{__float_as_uint(v.z), tag, __float_as_uint(v.w), tag}, pr, o + 16u);
+    } else {
+      st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, v), pr, p_off(rank, tile, tt));
+    }
+  };
 
   if constexpr (EPI) {
     if (epi_wave) {
@@ -748,7 +789,7 @@ void splitk_stream_kernel(GemmParams p) {
         else if (p.pdefer)
           pbuf[(k * NT + tt) * 64 + lane] = acc[tt];
         else
-          st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, acc[tt]), pr, p_off(rank, tile, tt));
+          put_partial(tile, tt, acc[tt]);
       }
     }
 #pragma unroll
@@ -814,8 +855,7 @@ void splitk_stream_kernel(GemmParams p) {
             if (k0 + j < ntl) {
               const int tile = col + cstride * (k0 + j);
 #pragma unroll
-              for (int tt = 0; tt < NT; ++tt)
-                st16_coherent_if(in_t(tt), __builtin_bit_cast(u32x4, hold[j][tt]), pr, p_off(rank, tile, tt));
+              for (int tt = 0; tt < NT; ++tt) put_partial(tile, tt, hold[j][tt]);
             }
           }
         }
@@ -858,6 +898,171 @@ void splitk_stream_kernel(GemmParams p) {
   // the result never depends on the peers being resident.
   auto tile_at = [&](int k) { return col + cstride * k; };
   auto owner_of = [&](int k) { return (k + gi) % S; };
+  constexpr uint32_t kArrivals = 0xFFu;  // arrival count bits of a counter
+  constexpr uint32_t kAbandon = 0x100u;  // the owner stopped waiting
+  const int k_first = ((rank - gi) % S + S) % S;  // first list position this rank owns
+  const int n_own = (ntl > k_first) ? (ntl - k_first + S - 1) / S : 0;
+
+  if (p.mailbox) {
+    // ---- mailbox hand-off ---------------------------------------------------
+    // Peers store tagged partials and do not wait; an owner polls the tagged
+    // data itself (one round trip after the last partial lands: no counter
+    // poll and no separate load of the partials), sums in rank order and
+    // stores C, and only then adds its arrival. The arrival counter serves
+    // the bounded wait alone: peers arrive once their stores are complete; an
+    // owner whose wait runs out arrives with the abandon bit (after storing
+    // its held partial); the arrival that brings the count to S resets it
+    // and, after an abandon, finishes the tile if it is a peer's.
+    const uint32_t tag = s_tag;
+    if (p.pdefer) {
+      __syncthreads();  // every tile's partial is in LDS
+      for (int k = wk; k < ntl; k += WK) {
+        if (owner_of(k) == rank) continue;
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) put_partial(tile_at(k), tt, pbuf[(k * NT + tt) * 64 + lane]);
+      }
+    }
+    // Polls the S partials of the tile at list position k until every tag is
+    // this launch's (each lane its own quad), then sums them in rank order
+    // and stores C: true; false if the deadline passes first. With `held`
+    // this rank's partial comes from LDS.
+    auto poll_finish = [&](int k, bool held, uint64_t deadline) -> bool {
+      const int tile = tile_at(k);
+      // Ranks whose data this lane still waits for, bit tt * 8 + r; a rank
+      // whose tags match keeps its values and is not loaded again.
+      uint32_t need = 0;
+      f32x4 v[NT][8];
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          v[tt][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (r < S) {
+            if (held && r == rank)
+              v[tt][r] = pbuf[(k * NT + tt) * 64 + lane];
+            else if (in_t(tt))
+              need |= 1u << (tt * 8 + r);
+          }
+        }
+      while (true) {
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            if (r < S) {
+              const bool want = (need >> (tt * 8 + r)) & 1u;
+              const uint32_t o = m_off(r, tile, tt);
+              const u32x4 a = ld16_coherent_if(want, pr, o);
+              const u32x4 b = ld16_coherent_if(want, pr, o + 16u);
+              if (want && a[1] == tag && a[3] == tag && b[1] == tag && b[3] == tag) {
+                v[tt][r] = f32x4{__uint_as_float(a[0]), __uint_as_float(a[2]), __uint_as_float(b[0]),
+                                 __uint_as_float(b[2])};
+                need &= ~(1u << (tt * 8 + r));
+              }
+            }
+          }
+        if (__builtin_amdgcn_ballot_w64(need != 0) == 0) {
+#pragma unroll
+          for (int tt = 0; tt < NT; ++tt) {
+            f32x4 sum = v[tt][0];
+#pragma unroll
+            for (int r = 1; r < 8; ++r)
+              if (r < S) sum += v[tt][r];
+            store_quad(co, in_t(tt), sum, c_el(tile, tt));
+          }
+          return true;
+        }
+        if (__builtin_amdgcn_s_memrealtime() > deadline) return false;
+        __builtin_amdgcn_s_sleep(8);
+      }
+    };
+    // A take-over only starts once every partial is complete, so its poll
+    // succeeds at once; it is still bounded (a record if it ever ran out).
+    constexpr uint64_t kTakeoverTicks = 1000000;  // 10 ms
+    auto take_over = [&](int k) {
+      handoff_order();
+      if (!poll_finish(k, false, __builtin_amdgcn_s_memrealtime() + kTakeoverTicks) && lane == 0)
+        note_timeout(p.health, (uint32_t)tile_at(k), 0xFFFFu, (uint32_t)kTakeoverTicks);
+    };
+
+    int k0 = 0, kstep = 1;
+    if constexpr (WK > 1) {
+      k0 = wk;
+      kstep = WK;
+    }
+    // Owned tiles first (their partials from the peers are, or will be,
+    // stored already): k = k_first + S*m, m spread over the waves.
+    const int my_own = (n_own > k0) ? (n_own - k0 + kstep - 1) / kstep : 0;
+    for (int i = 0; i < my_own; ++i) {
+      const int k = k_first + S * (k0 + kstep * i);
+      uint32_t* const cnt = cnt_of(tile_at(k));
+      const bool done = poll_finish(k, p.pdefer != 0, __builtin_amdgcn_s_memrealtime() + p.owner_wait);
+      uint32_t old = 0;
+      if (done) {
+        if (lane == 0) {
+          old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((old & kArrivals) == (uint32_t)(S - 1))
+            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        continue;
+      }
+      if (p.pdefer) {
+        // The tile may go to a peer now: this rank's partial, held in LDS
+        // so far, is stored and complete before the abandon.
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt) put_partial(tile_at(k), tt, pbuf[(k * NT + tt) * 64 + lane]);
+        wait_vmem_all();
+      }
+      if (lane == 0) {
+        old = __hip_atomic_fetch_add(cnt, 1u + kAbandon, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (p.owner_wait > 0) note_timeout(p.health, (uint32_t)tile_at(k), (uint32_t)rank, p.owner_wait);
+      }
+      old = __builtin_amdgcn_readfirstlane(old);
+      if ((old & kArrivals) == (uint32_t)(S - 1)) {
+        // Every peer had arrived: their partials are complete. Still ours.
+        if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        handoff_order();
+        if (!poll_finish(k, p.pdefer != 0, __builtin_amdgcn_s_memrealtime() + kTakeoverTicks) && lane == 0)
+          note_timeout(p.health, (uint32_t)tile_at(k), 0xFFFFu, (uint32_t)kTakeoverTicks);
+      }
+    }
+    // Peer arrivals, once every wave's partial stores are complete: this
+    // wave's share of the list, a lane per tile, tiles this rank owns left
+    // out (their owner arrives itself).
+    wait_vmem_all();
+    if constexpr (WK > 1) __syncthreads();
+    if (p.stamps) stamp[3] = __builtin_amdgcn_s_memrealtime();
+    const int my_tiles = (ntl > k0) ? (ntl - k0 + kstep - 1) / kstep : 0;
+    for (int j0 = 0; j0 < my_tiles; j0 += 64) {
+      const int j = j0 + lane;
+      bool take = false;
+      if (j < my_tiles) {
+        const int k = k0 + kstep * j;
+        if (owner_of(k) != rank) {
+          uint32_t* const cnt = cnt_of(tile_at(k));
+          const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((old & kArrivals) == (uint32_t)(S - 1)) {
+            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            take = (old & kAbandon) != 0;
+          }
+        }
+      }
+      uint64_t m = __builtin_amdgcn_ballot_w64(take);
+      while (m) {
+        const int b = __builtin_ctzll(m);
+        m &= m - 1;
+        take_over(k0 + kstep * (j0 + b));
+      }
+    }
+    if (tid == 0 && started_old == gridDim.x * gridDim.y - 1) {
+      // Every workgroup of this launch has read the epoch: the next launch's.
+      __hip_atomic_store(p.epoch + kCntStride, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.epoch, epoch0 + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    write_stamps();
+    return;
+  }
+
   if (p.pdefer) {
     // The partials held in LDS go out now, in one burst after the stream,
     // the workgroup's waves taking every WK-th tile (measured: mid-stream
@@ -882,9 +1087,6 @@ void splitk_stream_kernel(GemmParams p) {
     k0 = wk;
     kstep = WK;
   }
-  constexpr uint32_t kArrivals = 0xFFu;  // arrival count bits of a counter
-  constexpr uint32_t kAbandon = 0x100u;  // the owner stopped waiting
-
   // Sums the S partials of the tiles at list positions k0i (and k1i >= 0) in
   // rank order, one store each. With `held`, this rank's own partial is
   // taken from LDS (the owner's, which was never stored).
@@ -957,8 +1159,6 @@ void splitk_stream_kernel(GemmParams p) {
   }
 
   // Owned tiles: k = k_first + S*m, m spread over the waves like the list.
-  const int k_first = ((rank - gi) % S + S) % S;
-  const int n_own = (ntl > k_first) ? (ntl - k_first + S - 1) / S : 0;
   const int my_own = (n_own > k0) ? (n_own - k0 + kstep - 1) / kstep : 0;
   auto own_k = [&](int i) { return k_first + S * (k0 + kstep * i); };
   for (int i0 = 0; i0 < my_own; i0 += 64) {
@@ -1380,6 +1580,10 @@ bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L) {
     }
   }
   return false;
+}
+
+bool tactic_mailbox(const Tactic& t) {
+  return t.kind == 1 && kStreamShapes[t.shape].mode != kStreamEpilogue;
 }
 
 hipError_t launch_gemm(const Tactic& t, const GemmParams& p, hipStream_t s) {

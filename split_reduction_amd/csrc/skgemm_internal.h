@@ -35,6 +35,12 @@ struct GemmParams {
   // sum * c_scale saturated to +-448 (device/out.h).
   int out_e4m3;
   float c_scale;
+  // Persistent kernel's split-K hand-off: 0 arrival counter, 1 tagged
+  // mailbox (partials as (value, tag) pairs, 8 bytes per FP32 value; the tag
+  // comes from the epoch word at epoch[0], which the last workgroup to start
+  // a launch advances; epoch[kCntStride] counts the starts).
+  int mailbox;
+  uint32_t* epoch;
 };
 
 // Choices the library normally makes itself, which tests and tuning runs can
@@ -66,10 +72,12 @@ constexpr int kCntStride = 32;
 // owner rank, problem, ticks waited}.
 constexpr int kHealthRecords = 15;
 constexpr int kHealthWords = 8 + 8 * kHealthRecords;
-// Synchronisation words after the health words of a workspace (the chain
-// kernel's grid barrier: a generation, a global count and eight group
-// counts, one 128-byte line each).
-constexpr int kSyncWords = 10 * kCntStride;
+// Synchronisation words after the health words of a workspace, one 128-byte
+// line each: the chain kernel's grid barrier (a generation, a global count
+// and eight group counts), then the mailbox epoch and its start count.
+constexpr int kSyncWords = 12 * kCntStride;
+// The mailbox epoch words within them (lines 10 and 11).
+constexpr int kEpochWord = 10 * kCntStride;
 
 // Records one owner time-out (vector atomics and stores only).
 __device__ __forceinline__ void note_timeout(uint32_t* health, uint32_t group, uint32_t rank,
@@ -130,6 +138,11 @@ struct Tactic {
 // (L problems per launch); returns false if no instantiated configuration
 // fits (never for validated shapes).
 bool pick_tactic(int T, int N, int K, int S, int wf, Tactic* out, int L = 1);
+
+// Whether a launch with this configuration can use the tagged-mailbox
+// hand-off: the persistent kernel's deferred and storer organisations
+// (not its pipelined epilogue wave), single problems.
+bool tactic_mailbox(const Tactic& t);
 
 // Compute units of an MI355X: the grid a launch needs to occupy the chip.
 constexpr int kChipCUs = 256;

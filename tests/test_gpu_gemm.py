@@ -706,3 +706,83 @@ def test_health_records_timeouts(tune):
     assert h["timeouts"] >= 1 and len(h["records"]) == min(h["timeouts"], 15)
     assert_parity(bf16_bits(C), G.gemm_bf16_ref(x, w), K, "after time-outs")
     assert sk.skgemm_health()["timeouts"] == 0  # cleared
+
+
+MAILBOX_CASES = [(32, 2304, 7168, 8), (16, 4096, 4096, 8), (8, 8192, 8192, 4), (5, 4096, 4096, 8),
+                 (24, 1024, 4096, 8), (3, 4096, 1024, 2), (12, 16464, 4096, 8)]
+
+
+@pytest.mark.parametrize("shape", ["0", "1", "4", "5", "6"])
+@pytest.mark.parametrize("wait", ["0", "1", "10000"])
+def test_mailbox_handoff_bit_identical(shape, wait, tune):
+    """The tagged-mailbox hand-off sums the same partials in the same order
+    as the arrival counter: identical bits, within the oracle's bound, over
+    launches in a row (each with the next epoch's tag), with the owner wait
+    at its bound, at one tick (owners give up, peers take over) and at zero;
+    also with partials held in LDS or not (pdefer)."""
+    tune("kind", 1)
+    tune("stream", shape)
+    tune("owner_wait", wait)
+    ran = 0
+    for (T, N, K, S) in MAILBOX_CASES:
+        for pdefer in ("1", "0"):
+            tune("pdefer", pdefer)
+            tune("handoff", 0)
+            try:
+                tac = sk.skgemm_tactic_for(T, N, K, S)
+            except sk.SkgemmError:
+                continue
+            x, w = workloads.small_bf16_case(T, K, N, seed=9600 + T + S)
+            W = to_dev_bf16(w)
+            counter = run_bf16(x, None, S, W=W)
+            tune("handoff", 1)
+            tac = sk.skgemm_tactic_for(T, N, K, S)
+            assert tac["handoff"] == "mailbox", tac
+            log(f"mailbox shape={shape} wait={wait} pdefer={tac['pdefer']}: T={T} N={N} K={K} S={S}")
+            sk.skgemm_health()
+            for rep in range(3):
+                got = run_bf16(x, None, S, W=W)
+                assert np.array_equal(got, counter), f"rep {rep}: mailbox bits differ from the counter's"
+            h = sk.skgemm_health()
+            for (group, rank, problem, ticks) in h["records"]:
+                assert rank != 0xFFFF, "a take-over's poll ran out"
+                assert group < N // 16 and rank < S and ticks == int(wait)
+            if wait in ("0", "10000"):
+                assert h["timeouts"] == 0
+            assert_parity(got, G.gemm_bf16_ref(x, w), K, f"mailbox T={T} S={S}")
+            ran += 1
+    assert ran >= 4
+
+
+def test_mailbox_graph_replays_match_eager(tune):
+    """The mailbox tag comes from a device epoch word, not from the launch's
+    arguments: a captured launch replayed several times (eager mailbox calls
+    between) gives the eager bits every time."""
+    t = torch()
+    tune("handoff", 1)
+    T, N, K, S = 32, 4096, 7168, 8
+    tune("kind", 1)
+    log(f"mailbox graph T={T} N={N} K={K} S={S} tactic={sk.skgemm_tactic_for(T, N, K, S)}")
+    x, wb = workloads.small_bf16_case(T, K, N, seed=9650)
+    W, X = to_dev_bf16(wb), to_dev_bf16(x)
+    s = t.cuda.Stream()
+    sk.skgemm_reserve(T, N, S, s)
+    with t.cuda.stream(s):
+        eager = sentinel_bf16(T, N)
+        sk.skgemm_bf16(W, X, eager, T, N, K, S, s)
+    t.cuda.synchronize()
+    eager_bits = checked_bits(eager)
+    assert_parity(eager_bits, G.gemm_bf16_ref(x, wb), K, "mailbox eager")
+    C = sentinel_bf16(T, N)
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g, stream=s):
+        sk.skgemm_bf16(W, X, C, T, N, K, S, s)
+    for rep in range(4):
+        with t.cuda.stream(s):
+            C.fill_(float("nan"))
+            g.replay()
+            sk.skgemm_bf16(W, X, eager, T, N, K, S, s)  # an eager call between replays
+        t.cuda.synchronize()
+        assert np.array_equal(checked_bits(C), eager_bits), f"replay {rep}"
+        assert np.array_equal(checked_bits(eager), eager_bits), f"eager after replay {rep}"
+    del g

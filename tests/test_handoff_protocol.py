@@ -198,3 +198,81 @@ def test_wide_owner_arrives_first_exactly_one_finisher():
             for give_up_after in [None] + list(range(p_owner + 1, S + 1)):
                 f = run_wide(order, give_up_after, S, owner)
                 assert len(f) == 1, (S, order, give_up_after, f)
+
+
+# ---------------------------------------------------------------------------
+# Mailbox hand-off (the persistent kernel's alternative path): peers store
+# tagged partials, wait for them, then arrive; the owner polls the tagged
+# data itself, finishes, and only then arrives. A give-up is an arrival with
+# the abandon bit (one atomic add of 1 + ABANDON). Whoever's arrival brings
+# the count to S resets the counter; if the abandon bit is set and that is not
+# the owner, it finishes the tile. Every order of the S-1 peer arrivals and
+# the owner's (normal or give-up) arrival must give exactly one finisher and
+# exactly one reset, and a taker must see every partial.
+# ---------------------------------------------------------------------------
+
+
+def run_mailbox(peer_order, owner_pos, gives_up, S):
+    """peer_order: the S-1 peers' arrival order; owner_pos: how many peer
+    arrivals precede the owner's; gives_up: the owner's wait runs out (its
+    data poll did not see every tag) instead of finishing first."""
+    cnt = 0
+    finishers, resets = [], 0
+    visible = set()
+    owner = 0
+    events = list(peer_order[:owner_pos]) + ["owner"] + list(peer_order[owner_pos:])
+    for ev in events:
+        if ev == "owner":
+            if gives_up:
+                visible.add(owner)  # its held partial is stored and complete first
+                old, cnt = cnt, cnt + 1 + ABANDON
+                if (old & ARRIVALS) == S - 1:
+                    finishers.append(("owner", set(visible)))  # all peers' data is there
+                    resets += 1
+                    cnt = 0
+            else:
+                # the data poll saw every peer's tag: all peers stored
+                finishers.append(("owner", set(range(S))))
+                old, cnt = cnt, cnt + 1
+                if (old & ARRIVALS) == S - 1:
+                    resets += 1
+                    cnt = 0
+        else:
+            visible.add(ev)  # stores complete before the arrival
+            old, cnt = cnt, cnt + 1
+            if (old & ARRIVALS) == S - 1:
+                if old & ABANDON:
+                    finishers.append((("taker", ev), set(visible)))
+                resets += 1
+                cnt = 0
+    return finishers, resets, cnt
+
+
+def test_mailbox_protocol_one_finisher_one_reset():
+    for S in (2, 3, 4, 8):
+        peers = tuple(range(1, S))
+        orders = itertools.permutations(peers) if S <= 4 else [peers, peers[::-1]]
+        for order in orders:
+            for owner_pos in range(S):
+                # (a normal finish needs every peer's tag, not its arrival:
+                # peers store, and may arrive after the owner has finished)
+                for gives_up in (False, True):
+                    f, resets, cnt = run_mailbox(order, owner_pos, gives_up, S)
+                    assert len(f) == 1, (S, order, owner_pos, gives_up, f)
+                    assert resets == 1 and cnt == 0, (S, order, owner_pos, gives_up, resets, cnt)
+                    assert f[0][1] == set(range(S)), (S, order, owner_pos, gives_up, f)
+
+
+def test_mailbox_reset_by_owner_race_would_lose_a_tile():
+    """The planted alternative: the owner does not arrive and the last peer
+    resets. An owner that then gives up finds the count at zero and cannot tell
+    'nobody arrived' from 'everyone arrived and reset': the tile is lost."""
+    S = 4
+    cnt = 0
+    for _ in range(S - 1):  # every peer arrives; the last one resets
+        old, cnt = cnt, cnt + 1
+        if (old & ARRIVALS) == S - 2:
+            cnt = 0
+    old, cnt = cnt, cnt | ABANDON  # the owner's late give-up
+    owner_finishes = (old & ARRIVALS) == S - 1
+    assert not owner_finishes and cnt == ABANDON  # nobody finishes; the counter stays dirty
