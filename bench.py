@@ -682,6 +682,109 @@ def mfma_summary(path: str, names: list) -> list:
     return outs
 
 
+# Phase names of the per-workgroup stamps each kernel kind writes
+# (skgemm_set_timeline).
+PHASES = {
+    "stream": ["entry", "X staged", "stream done", "own partials stored", "exit", "arrivals done",
+               "owned polls done"],
+    "cluster": ["entry", "loads issued", "wave 0 stream done", "sums in LDS", "exit"],
+    "wide": ["entry", "first X chunk staged", "stream done", "partial stored", "exit"],
+}
+
+
+def phases(names: list, overrides: list, out_dir: str, launches: int = 3) -> None:
+    """Per-workgroup phase stamps of single cold launches (eager, one stream),
+    pooled over `launches` launches, each relative to its earliest entry.
+    `overrides` are NAME=VALUE library overrides (skgemm_set_override), e.g.
+    kind=1 to run a workload on the persistent kernel. Writes
+    phases_<workload>[_<overrides>].md with the command under out_dir
+    (profiles/ by default)."""
+    import torch
+
+    import split_reduction_amd as sk
+
+    sk.lib()
+    pins = [o.split("=") for o in overrides]
+    for k, v in pins:
+        sk.skgemm_set_override(k, int(v))
+    suffix = "".join(f"_{k}{v}" for k, v in pins)
+    fmt = {"bf16": 0, "mxfp4": 1, "mxfp8": 2}
+    wsweep = None
+    try:
+        for name in names:
+            wl = workloads.get(name)
+            host_w = None
+            if is_sweep(name):
+                if wsweep is None:
+                    wsweep = workloads.gen_w_bf16(workloads.sweep_workload(1))
+                host_w = wsweep
+            case = Case(wl, host_w)
+            tac = sk.skgemm_tactic_for(wl.T, wl.N, wl.K, wl.split_k, fmt[wl.kind])
+            kind = tac["kind"]
+            grid = tac["grid"]
+            stream = torch.cuda.Stream()
+            sk.skgemm_reserve(wl.T, wl.N, wl.split_k, stream)
+            buf = torch.zeros(grid * 8, dtype=torch.int64, device="cuda:0")
+            warm = 2 * case.copies
+            with torch.cuda.stream(stream):
+                for i in range(warm):
+                    case.launch(i, stream)
+            stream.synchronize()
+            pooled, spans = [], []
+            for r in range(launches):
+                buf.zero_()
+                torch.cuda.synchronize()
+                sk.skgemm_set_timeline(buf, buf.numel())
+                try:
+                    with torch.cuda.stream(stream):
+                        case.launch(warm + r, stream)  # the copy launched least recently
+                    stream.synchronize()
+                finally:
+                    sk.skgemm_set_timeline(None, 0)
+                st = buf.view(grid, 8).cpu().numpy().astype(np.float64)
+                t0 = st[:, 0].min()
+                rel = np.where(st > 0, (st - t0) * 0.01, np.nan)  # microseconds
+                pooled.append(rel)
+                spans.append(float(np.nanmax(rel[:, 4])))
+            allst = np.concatenate(pooled)
+            cmd = "python bench.py --phases " + name + "".join(f" --override {k}={v}" for k, v in pins)
+            lines = [f"# Phase stamps: {name}{' (' + ', '.join(overrides) + ')' if overrides else ''}", "",
+                     f"Kernel sources `{kernel_source_hash()}`; tactic {json.dumps(tac)}.", "",
+                     f"Command: `{cmd}` (eager single launches on cold weights, device clock "
+                     f"s_memrealtime at 100 MHz; {launches} launches pooled, each relative to its "
+                     f"earliest workgroup entry; wave 0's view per workgroup).", "",
+                     "Launch spans (first entry to last exit): "
+                     + ", ".join(f"{v:.2f}" for v in spans) + " us", "",
+                     "| phase | min | p10 | median | p90 | max |", "|---|---|---|---|---|---|"]
+            names_k = PHASES.get(kind, [f"stamp {i}" for i in range(5)])
+            order = [0, 1, 2, 3, 5, 6, 4] if len(names_k) == 7 else list(range(len(names_k)))
+            for j in order:  # in time order
+                ph = names_k[j]
+                v = allst[:, j]
+                v = v[~np.isnan(v)]
+                if v.size == 0:
+                    continue
+                lines.append(f"| {ph} | {v.min():.2f} | {np.percentile(v, 10):.2f} | {np.median(v):.2f} | "
+                             f"{np.percentile(v, 90):.2f} | {v.max():.2f} |")
+            xcd = np.tile(np.arange(grid) % 8, launches)
+            lines += ["", "Per XCD (block index mod 8): median and max of the stream-done stamp, max exit (us):", "",
+                      "| XCD | median stream done | max stream done | max exit |", "|---|---|---|---|"]
+            for x in range(8):
+                m = xcd == x
+                lines.append(f"| {x} | {np.nanmedian(allst[m, 2]):.2f} | {np.nanmax(allst[m, 2]):.2f} | "
+                             f"{np.nanmax(allst[m, 4]):.2f} |")
+            text = "\n".join(lines) + "\n"
+            print(text, flush=True)
+            os.makedirs(out_dir, exist_ok=True)
+            with open(os.path.join(out_dir, f"phases_{name}{suffix}.md"), "w") as f:
+                f.write(text)
+            del case, buf
+            torch.cuda.empty_cache()
+    finally:
+        if pins:
+            sk.clear_overrides()
+
+
 # ---------------------------------------------------------------------------
 
 
@@ -712,7 +815,16 @@ def main() -> None:
                     help="summarise an MfmaUtil / MfmaFlopsBF16 counter pass of --pmc-run and exit")
     ap.add_argument("--pmc-summary", nargs="+", metavar=("DIR", "WORKLOAD"),
                     help="summarise the FETCH_SIZE / WRITE_SIZE passes under DIR and exit")
+    ap.add_argument("--phases", nargs="+", metavar="WORKLOAD",
+                    help="per-workgroup phase stamps of single cold launches, written to profiles/; exit")
+    ap.add_argument("--override", action="append", default=[], metavar="KNOB=VALUE",
+                    help="with --phases: a library override (skgemm_set_override) for the run")
+    ap.add_argument("--out", default=os.path.join(ROOT, "profiles"), metavar="DIR",
+                    help="with --phases: where the summaries go (default profiles/)")
     args = ap.parse_args()
+    if args.phases:
+        phases(pmc_names(args.phases), args.override, args.out)
+        return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], pmc_names(args.pmc_summary[1:]))
         return

@@ -332,9 +332,14 @@ SKGEMM_API int skgemm_tactic_for(int T, int N, int K, int split_k, int weight_fo
  * skgemm_set_timeline: opt-in phase stamps of the persistent stream kernel
  * (page vllm.models.deepseek_v41.amd.mono.common.ops, module note and
  * memrealtime: timeline phase stamps from s_memrealtime, the 100 MHz device
- * clock). While set, every workgroup w of a stream-kernel launch writes five
- * uint64 clock values to buf[8*w .. 8*w+4]: kernel entry, X staged in LDS,
- * weight stream done, own partial stores complete, exit. Device memory,
+ * clock). While set, every workgroup w of a stream-kernel launch writes
+ * uint64 clock values to buf[8*w .. 8*w+7]: kernel entry, X staged in LDS,
+ * weight stream done, own partial stores complete, exit, then (counter
+ * hand-off, as its wave 0 sees it; 0 elsewhere) arrivals done and the owned
+ * tiles' polls done, and 0. The cluster kernel writes entry, first loads
+ * issued, wave 0's stream done, every wave's sums in LDS, exit; the wide
+ * kernel entry, first X chunk staged, stream done, its column's partial
+ * stored, exit. Device memory,
  * caller-owned, 8-byte aligned; `capacity` is its length in uint64. Launches
  * whose grid needs more than capacity/8 workgroups write nothing. Pass
  * buf = NULL to turn stamping off (the default). Process-wide setting.

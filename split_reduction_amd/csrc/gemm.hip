@@ -423,7 +423,10 @@ void splitk_stream_kernel(GemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   __shared__ uint32_t s_tag;  // mailbox tag of this launch
 
-  uint64_t stamp[5];  // optional phase stamps (s_memrealtime, 100 MHz)
+  // Optional phase stamps (s_memrealtime, 100 MHz): entry, X staged, stream
+  // done, own partial stores complete, exit, and in the counter hand-off the
+  // arrivals done and the owned tiles' polls done (wave 0's view).
+  uint64_t stamp[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   stamp[0] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -605,7 +608,7 @@ void splitk_stream_kernel(GemmParams p) {
       stamp[4] = __builtin_amdgcn_s_memrealtime();
       const rsrc_t sr8 = make_rsrc(p.stamps + (size_t)blockIdx.x * 8, 64);
 #pragma unroll
-      for (int i = 0; i < 5; ++i)
+      for (int i = 0; i < 8; ++i)
         st8_if(true, u32x2{(uint32_t)stamp[i], (uint32_t)(stamp[i] >> 32)}, sr8, 8u * i);
     }
   };
@@ -1158,6 +1161,7 @@ void splitk_stream_kernel(GemmParams p) {
     finish_mask(__builtin_amdgcn_ballot_w64(take), [&](int b) { return k0 + kstep * (j0 + b); }, false);
   }
 
+  if (p.stamps) stamp[5] = __builtin_amdgcn_s_memrealtime();
   // Owned tiles: k = k_first + S*m, m spread over the waves like the list.
   const int my_own = (n_own > k0) ? (n_own - k0 + kstep - 1) / kstep : 0;
   auto own_k = [&](int i) { return k_first + S * (k0 + kstep * i); };
@@ -1205,6 +1209,7 @@ void splitk_stream_kernel(GemmParams p) {
       __builtin_amdgcn_s_sleep(2);
     }
     if (ready) __hip_atomic_store(cnt_of(tile), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (p.stamps) stamp[6] = __builtin_amdgcn_s_memrealtime();
     handoff_order();  // the partial loads stay after the poll that saw every arrival
     finish_mask(__builtin_amdgcn_ballot_w64(ready), [&](int b) { return own_k(i0 + b); }, p.pdefer != 0);
   }

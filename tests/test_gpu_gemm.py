@@ -658,7 +658,8 @@ def test_batched_mxfp4_and_oversized_grid():
 
 def test_timeline_stamps(tune):
     """Opt-in phase stamps: five non-decreasing device-clock values per
-    workgroup, results unchanged, and nothing written once turned off."""
+    workgroup, the counter hand-off's two (where reached) between the own
+    stores and the exit, results unchanged, nothing written once turned off."""
     tune("kind", "1")
     t = torch()
     w = workloads.WORKLOADS["bf16_t8_k7168_n2048"]
@@ -674,8 +675,13 @@ def test_timeline_stamps(tune):
     finally:
         sk.skgemm_set_timeline(None, 0)
     st = buf.view(tac["grid"], 8).cpu().numpy()
-    assert np.all(st[:, :5] > 0) and np.all(st[:, 5:] == 0)
+    assert np.all(st[:, :5] > 0) and np.all(st[:, 7] == 0)
     assert np.all(np.diff(st[:, :5], axis=1) >= 0)
+    for j in (5, 6):  # arrivals done, owned polls done: 0 where not reached
+        m = st[:, j] > 0
+        assert np.all(st[m, j] >= st[m, 3]) and np.all(st[m, j] <= st[m, 4])
+    m = (st[:, 5] > 0) & (st[:, 6] > 0)
+    assert np.all(st[m, 6] >= st[m, 5])
     span_us = (st[:, 4].max() - st[:, 0].min()) * 0.01
     log(f"  workgroup span {span_us:.2f} us")
     assert 0 < span_us < 1e4
