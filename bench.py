@@ -480,10 +480,18 @@ def trace_summary(path: str, steps: int, warmup: int) -> None:
         else:
             segs.append((key, [dur]))
     print("run  calls   avg(us)   med(us)   min(us)     grid  kernel")
+    singles = {}  # one-dispatch runs (launches alternating between kernels), grouped by kernel
     for i, ((name, grid), durs) in enumerate(segs):
         d = np.array(durs)
-        short = name.replace("void skg::", "").replace("(skg::GemmParams)", "")
+        short = name.replace("void skg::", "").replace("(skg::GemmParams)", "").replace("(skg::ChainParams)", "")
+        if len(d) == 1:
+            singles.setdefault((short, grid), []).append(d[0])
+            continue
         print(f"{i:3d} {len(d):6d} {d.mean():9.3f} {np.median(d):9.3f} {d.min():9.3f} {grid:>8}  {short}")
+    for (short, grid), durs in singles.items():
+        d = np.array(durs)
+        print(f"  * {len(d):6d} {d.mean():9.3f} {np.median(d):9.3f} {d.min():9.3f} {grid:>8}  {short}"
+              "  (one-dispatch runs, alternating kernels)")
     per_pass = warmup + 2 * steps
     head = [s for s in segs if len(s[1]) >= 2 * per_pass]
     if head:
