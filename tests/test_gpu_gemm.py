@@ -230,6 +230,55 @@ def test_mxfp8_integer_operands_bit_exact(S):
     assert np.array_equal(F.bf16_bits_to_f64(c), F.bf16_bits_to_f64(F.f32_to_bf16_rne(exact.astype(np.float32))))
 
 
+# Unfolded block-scaled tiles of the cluster kernel (T = 9..32) at slices of
+# several lengths. The scales change from block to block, so a scale taken
+# from the wrong block, row or rank slice changes the exact result.
+BLOCK_SCALE_CASES = [
+    # (T, K, S): rank slice ks = K / S
+    (16, 1024, 2),   # ks 512
+    (16, 1280, 2),   # ks 640
+    (9, 3584, 4),    # ks 896
+    (16, 4096, 2),   # ks 2048
+    (20, 4352, 2),   # ks 2176, two token tiles
+    (16, 768, 2),    # ks 384
+    (12, 1152, 2),   # ks 576: MXFP8 only (MXFP4 needs K % (128 * split_k) == 0)
+]
+
+
+def _block_scale_case(fmt, T, K, N, seed):
+    rng = np.random.default_rng(seed)
+    x = workloads.to_bf16_bits(rng.integers(-3, 4, size=(T, K)).astype(np.float32))
+    ws = rng.integers(125, 130, size=(N, K // 32), dtype=np.uint8)  # 2^-2 .. 2^2 per block
+    if fmt == "mxfp4":
+        wq = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+        return x, wq, ws, G.gemm_mxfp4_ref(x, wq, ws)
+    ints = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0xB8, 0xC0, 0xC4, 0x80], dtype=np.uint8)
+    wq8 = rng.choice(ints, size=(N, K))
+    return x, wq8, ws, G.gemm_mxfp8_ref(x, wq8, ws)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("T,K,S", BLOCK_SCALE_CASES)
+def test_cluster_block_scales_bit_exact(fmt, T, K, S, tune):
+    """Integer activations, small-integer weights and per-block power-of-two
+    scales: every product and partial sum is exact in FP32, so the bf16
+    output is the RNE rounding of the exact result, bit for bit."""
+    N = 256
+    step = 128 if fmt == "mxfp4" else 64
+    if (K // S) % step:
+        pytest.skip("slice not a whole number of load steps")
+    tune("kind", 2)
+    wf = 1 if fmt == "mxfp4" else 2
+    tac = sk.skgemm_tactic_for(T, N, K, S, wf)
+    log(f"{fmt} block scales T={T} K={K} S={S} ks={K // S} tactic={tac}")
+    assert tac["kind"] == "cluster" and tac["fold"] == 1
+    x, wq, ws, exact = _block_scale_case(fmt, T, K, N, seed=7100 + T + K + S + wf)
+    assert np.max(np.abs(exact)) < 2**22
+    c = run_mxfp4(x, wq, ws, S) if fmt == "mxfp4" else run_mxfp8(x, wq, ws, S)
+    want = F.f32_to_bf16_rne(exact.astype(np.float32))
+    assert np.array_equal(F.bf16_bits_to_f64(c), F.bf16_bits_to_f64(want))
+
+
 def test_mxfp8_batched_and_workload():
     t = torch()
     T, N, K, S, L = 16, 512, 2048, 4, 3
