@@ -629,12 +629,12 @@ def pmc_summary(path: str, names: list) -> list:
             "algorithmic_bytes_per_launch": algo,
             "commands": [
                 "cd /tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE --output-format csv "
-                "-d $R/gpurun_out/pmc/fetch -o fetch -- python3 $R/bench.py --pmc-run all",
+                "-d $OUT/pmc/fetch -o fetch -- python3 $R/bench.py --pmc-run all",
                 "cd /tmp && timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE --output-format csv "
-                "-d $R/gpurun_out/pmc/write -o write -- python3 $R/bench.py --pmc-run all",
-                "python bench.py --pmc-summary gpurun_out/pmc all",
+                "-d $OUT/pmc/write -o write -- python3 $R/bench.py --pmc-run all",
+                "python bench.py --pmc-summary $OUT/pmc all",
             ],
-            "note": (f"R is the repository root. Counters are per dispatch: {PMC_LAUNCHES} launches of each "
+            "note": (f"R is the repository root, OUT any output directory. Counters are per dispatch: {PMC_LAUNCHES} launches of each "
                      f"workload on rotated weights, then {PMC_COPIES} copies of {COPY_BYTES >> 20} MiB whose "
                      "counter readings calibrate KiB per byte moved."),
         }
@@ -649,7 +649,7 @@ def pmc_summary(path: str, names: list) -> list:
         f.write(f"Kernel sources: `{sha}`. Counters calibrated on {PMC_COPIES} plain device copies of "
                 f"{COPY_BYTES >> 20} MiB: FETCH_SIZE reads {fetch_factor:.4f} KiB x 1024 per byte read, "
                 f"WRITE_SIZE {write_factor:.4f} per byte written.\n\n")
-        f.write("Commands (R = repository root):\n\n")
+        f.write("Commands (R = repository root, OUT any output directory):\n\n")
         for c in outs[0]["commands"]:
             f.write(f"    {c}\n")
         f.write("\n" + "\n".join(table) + "\n")
@@ -679,10 +679,10 @@ def mfma_summary(path: str, names: list) -> list:
         table.append(f"| {name} | `{kname}` | {u:.2f} | {fl:.4g} | {wl.flops():.4g} | {fl / wl.flops():.3f} |")
     with open(os.path.join(ROOT, "profiles", "mfma_summary.md"), "w") as f:
         f.write("# Matrix-core use per launch (rocprofv3 MfmaUtil, MfmaFlopsBF16)\n\n")
-        f.write(f"Kernel sources: `{sha}`. Command (R = repository root):\n\n"
+        f.write(f"Kernel sources: `{sha}`. Command (R = repository root, OUT any output directory):\n\n"
                 "    cd /tmp && timeout -s KILL 300 rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 --output-format csv "
-                "-d $R/gpurun_out/mfma -o mfma -- python3 $R/bench.py --pmc-run all\n"
-                "    python bench.py --mfma-summary gpurun_out/mfma all\n\n"
+                "-d $OUT/mfma -o mfma -- python3 $R/bench.py --pmc-run all\n"
+                "    python bench.py --mfma-summary $OUT/mfma all\n\n"
                 "Executed MFMA flops exceed 2*T*N*K by the token padding to 16 and, in folded tiles, by "
                 "the off-diagonal blocks that are computed and not read.\n\n")
         f.write("\n".join(table) + "\n")
