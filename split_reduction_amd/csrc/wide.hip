@@ -40,7 +40,13 @@ namespace {
 
 constexpr int kWideWaves = 8;                // wave columns per workgroup
 constexpr int kWideRows = 32 * kWideWaves;   // weight rows per workgroup
-constexpr int wide_kc(int nt) { return nt <= 4 ? 512 : 256; }  // K elements per X chunk
+// bf16 tiles of up to 64 tokens keep three activation chunks in LDS with a
+// handshake (below); the others two, closed by a barrier.
+constexpr bool wide_drift(int nt, int wf) { return wf == kBf16 && nt <= 4; }
+constexpr int wide_kc(int nt, int wf) {  // K elements per X chunk
+  return wide_drift(nt, wf) ? 256 : (nt <= 4 ? 512 : 256);
+}
+constexpr int wide_nbuf(int nt, int wf) { return wide_drift(nt, wf) ? 3 : 2; }
 
 }  // namespace
 
@@ -53,7 +59,9 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
   constexpr int THREADS = 64 * kWideWaves;
   constexpr int SUBS = MX ? LK / 8 : 1;       // MFMA K-steps per load step
   constexpr int STEP_K = MX ? 4 * LK : 32;    // K elements of one load step
-  constexpr int KC = wide_kc(NT);
+  constexpr int KC = wide_kc(NT, WF);
+  constexpr bool DRIFT = wide_drift(NT, WF);
+  constexpr int NB = wide_nbuf(NT, WF);  // activation chunk buffers in LDS
   constexpr int CS = KC / STEP_K;             // load steps per chunk
   // A ring slot holds two load steps: per 16-row group, rows 0-7 and rows
   // 8-15 over both steps' 64-byte windows, one whole 128-byte line per row
@@ -136,18 +144,18 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
   constexpr int XP = (PIECES + THREADS - 1) / THREADS;  // pieces per thread per chunk
   auto x_slot = [&](int j, int s, int gg, int t) -> int { return ((j * SUBS + s) * 4 + gg) * TP + t; };
   u32x4 xreg[XP];
-  auto x_load = [&](int c) {
+  auto x_load = [&](int c, u32x4 (&dst)[XP]) {
     const int k0 = kbase + c * KC;
 #pragma unroll
     for (int b = 0; b < XP; ++b) {
       const int pc = tid + b * THREADS;
       const int t = pc / (KC / 8);
       const int k = (pc % (KC / 8)) * 8;
-      xreg[b] = ld16_if(pc < PIECES && t < T, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(k0 + k)) * 2u);
+      dst[b] = ld16_if(pc < PIECES && t < T, xr, ((uint32_t)t * (uint32_t)K + (uint32_t)(k0 + k)) * 2u);
     }
   };
-  auto x_store = [&](int c) {
-    uint8_t* buf = smem + (c & 1) * CHUNK_BYTES;
+  auto x_store = [&](int c, const u32x4 (&src)[XP]) {
+    uint8_t* buf = smem + (c % NB) * CHUNK_BYTES;
 #pragma unroll
     for (int b = 0; b < XP; ++b) {
       const int pc = tid + b * THREADS;
@@ -160,7 +168,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
         } else {
           j = k / 32; s2 = 0; gg = (k % 32) / 8;
         }
-        *reinterpret_cast<u32x4*>(buf + x_slot(j, s2, gg, t) * 16) = xreg[b];
+        *reinterpret_cast<u32x4*>(buf + x_slot(j, s2, gg, t) * 16) = src[b];
       }
     }
   };
@@ -173,7 +181,7 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
 
   // Slot jp of chunk c: load steps 2*jp and 2*jp + 1 of the chunk.
   auto compute = [&](int slot, int c, int jp) {
-    const uint8_t* buf = smem + (c & 1) * CHUNK_BYTES;
+    const uint8_t* buf = smem + (c % NB) * CHUNK_BYTES;
     u32x4 a[RG][2];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) line_pair_to_operands(ring[slot][rg][0], ring[slot][rg][1], a[rg][0], a[rg][1]);
@@ -201,28 +209,92 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
     }
   };
 
-  // Prologue: chunk 0's X first (its LDS writes then wait only for X), the
-  // weight ring behind it.
-  x_load(0);
+  if constexpr (!DRIFT) {
+    // Prologue: chunk 0's X first (its LDS writes then wait only for X), the
+    // weight ring behind it.
+    x_load(0, xreg);
 #pragma unroll
-  for (int s = 0; s < D; ++s) issue(s, s);
-  x_store(0);
-  __syncthreads();
-  stamp[1] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
+    for (int s = 0; s < D; ++s) issue(s, s);
+    x_store(0, xreg);
+    __syncthreads();
+    stamp[1] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
 
-  for (int c = 0; c < nchunks; ++c) {
-    const bool next = c + 1 < nchunks;
-    if (next) x_load(c + 1);
+    for (int c = 0; c < nchunks; ++c) {
+      const bool next = c + 1 < nchunks;
+      if (next) x_load(c + 1, xreg);
 #pragma unroll
-    for (int jp = 0; jp < CS2; ++jp) {
-      const int slot = jp % D;
-      compute(slot, c, jp);
-      issue(slot, c * CS2 + jp + D);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int jp = 0; jp < CS2; ++jp) {
+        const int slot = jp % D;
+        compute(slot, c, jp);
+        issue(slot, c * CS2 + jp + D);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (next) {
+        x_store(c + 1, xreg);
+        __syncthreads();
+      }
     }
-    if (next) {
-      x_store(c + 1);
-      __syncthreads();
+  } else {
+    // Three chunk buffers and a handshake instead of a barrier per chunk:
+    // chunk c sits in buffer c % 3, a wave computes it once all eight waves
+    // have stored their part of it (ready), and a wave stores chunk c + 2 at
+    // the end of chunk c once all eight have finished chunk c - 1, the
+    // buffer's previous user (done). A wave can so run up to a chunk ahead
+    // of the slowest one; with one barrier per chunk every chunk waited for
+    // the slowest wave (measured: a timing copy without those barriers ran
+    // 117.5 against 127.4 us at T=64, K=N=16384). Both counts only grow: the
+    // u-th use of a buffer (u = c / 3) is ready at 8 (u + 1) stores and free
+    // again at 8 (u + 1) finished computes. A wait that runs out (not
+    // expected: the waves of a workgroup run together) is recorded in the
+    // health words and the wave goes on.
+    __shared__ uint32_t chunk_ready[3], chunk_done[3];
+    auto signal = [&](uint32_t* ctr) {
+      if (lane == 0) __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+    auto wait_at_least = [&](uint32_t* ctr, uint32_t target, uint32_t what) {
+      const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + 1000000;  // 10 ms
+      while (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        if (__builtin_amdgcn_s_memrealtime() > deadline) {
+          if (lane == 0) note_timeout(p.health, 0xFFFFFFFEu, what, 1000000u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    };
+    // Prologue: chunks 0 and 1, their X loads ahead of the weight ring (so
+    // their LDS writes wait only for X), made visible by one barrier.
+    u32x4 xreg1[XP];
+    x_load(0, xreg);
+    if (nchunks > 1) x_load(1, xreg1);
+#pragma unroll
+    for (int s = 0; s < D; ++s) issue(s, s);
+    x_store(0, xreg);
+    if (nchunks > 1) x_store(1, xreg1);
+    if (tid < 3) {
+      chunk_ready[tid] = tid < 2 ? 8u : 0u;  // chunks 0 and 1 are stored before the barrier
+      chunk_done[tid] = 0u;
+    }
+    __syncthreads();
+    stamp[1] = p.stamps ? __builtin_amdgcn_s_memrealtime() : 0;
+
+    for (int c = 0; c < nchunks; ++c) {
+      const bool ahead = c + 2 < nchunks;
+      if (ahead) x_load(c + 2, xreg);
+      if (c >= 2) wait_at_least(&chunk_ready[c % 3], 8u * (uint32_t)(c / 3 + 1), (uint32_t)c);
+#pragma unroll
+      for (int jp = 0; jp < CS2; ++jp) {
+        const int slot = jp % D;
+        compute(slot, c, jp);
+        issue(slot, c * CS2 + jp + D);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      signal(&chunk_done[c % 3]);  // this wave's reads of chunk c are complete
+      if (ahead) {
+        // Buffer (c + 2) % 3 last held chunk c - 1.
+        if (c >= 1) wait_at_least(&chunk_done[(c + 2) % 3], 8u * (uint32_t)((c - 1) / 3 + 1), (uint32_t)c);
+        x_store(c + 2, xreg);
+        signal(&chunk_ready[(c + 2) % 3]);
+      }
     }
   }
 
@@ -393,7 +465,7 @@ bool wide_fits(int T, int N, int ks, int S, int wf, Tactic* t) {
   const bool mx = wf != kBf16;
   const int nt = (T + 15) / 16;
   if (nt < 3 || nt > 8 || N % kWideRows || ks <= 0) return false;
-  const int kc = wide_kc(nt);
+  const int kc = wide_kc(nt, wf);
   if (ks % kc) return false;
   (void)mx;
   t->kind = 3;
@@ -406,7 +478,7 @@ bool wide_fits(int T, int N, int ks, int S, int wf, Tactic* t) {
   t->kc = kc;
   t->tile_n = kWideRows;
   t->threads = 64 * kWideWaves;
-  t->lds = 2 * 16 * nt * kc * 2;
+  t->lds = wide_nbuf(nt, wf) * 16 * nt * kc * 2;
   t->grid = (N / kWideRows) * S;
   t->shape = 0;
   t->fold = 1;
