@@ -584,6 +584,24 @@ def test_wide_integer_exact(S, tune):
         assert np.array_equal(F.bf16_bits_to_f64(run_bf16(x, w, S)), F.bf16_bits_to_f64(want))
 
 
+# bf16 wide tiles of up to 64 tokens pass activation chunks of 256 elements
+# through three LDS buffers with a handshake; n chunks per rank slice covers
+# the prologue's one and two chunks, a partial turn of the buffers and many.
+@pytest.mark.parametrize("T,n,S", [(33, 1, 1), (64, 1, 4), (48, 2, 2), (40, 3, 1), (64, 5, 2), (57, 16, 4)])
+def test_wide_chunk_handshake_integer_exact(T, n, S, tune):
+    tune("kind", "3")
+    N, K = 512, 256 * n * S
+    tac = sk.skgemm_tactic_for(T, N, K, S)
+    log(f"wide handshake T={T} chunks={n} S={S} K={K} tactic={tac}")
+    assert tac["kind"] == "wide" and tac["kc"] == 256
+    x, w = workloads.integer_bf16_case(T, K, N, seed=9300 + T + n + S, mag=2)
+    exact = G.gemm_bf16_ref(x, w)
+    assert np.max(np.abs(exact)) < 2**24
+    want = F.f32_to_bf16_rne(exact.astype(np.float32))
+    for rep in range(2):
+        assert np.array_equal(F.bf16_bits_to_f64(run_bf16(x, w, S)), F.bf16_bits_to_f64(want)), f"rep {rep}"
+
+
 @pytest.mark.parametrize("shape", ["0", "6"])
 def test_partials_held_in_lds_bit_identical(shape, tune):
     """The persistent kernel holds tile partials in LDS until its stream ends
