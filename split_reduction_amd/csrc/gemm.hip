@@ -467,8 +467,11 @@ void splitk_stream_kernel(GemmParams p) {
   const rsrc_t sr = MX ? make_rsrc(p.wscale, (uint32_t)N * (uint32_t)(K / 32)) : wr;
   const rsrc_t xr = make_rsrc(p.x, (uint32_t)T * (uint32_t)K * 2u);
   const COut co = make_cout(p);
-  // Partials: FP32 [S, T, N]; in the mailbox hand-off each value is an
-  // 8-byte (value, tag) pair.
+  // Partials: FP32, tile-major [S, N/16, T, 16]: rank r's partial of one
+  // 16-row tile is T x 64 contiguous bytes, so a wave's store or read-back
+  // of a token tile covers whole lines (with [S, T, N] it is 16 runs of 64
+  // bytes, N * 4 bytes apart). In the mailbox hand-off each value is an
+  // 8-byte (value, tag) pair, token-major [S, T, N].
   const rsrc_t pr = make_rsrc(p.part, (uint32_t)S * (uint32_t)T * (uint32_t)N * (p.mailbox ? 8u : 4u));
   // Arrival counter of a 16-row tile: one 128-byte line each, so the S
   // ranks' arrivals and the owner's polls of one tile meet no other tile's
@@ -619,8 +622,8 @@ void splitk_stream_kernel(GemmParams p) {
     return (uint32_t)(tt * 16 + li) * (uint32_t)N + (uint32_t)(tile * 16 + 4 * g);
   };
   auto p_off = [&](int r, int tile, int tt) -> uint32_t {
-    return (((uint32_t)r * (uint32_t)T + (uint32_t)(tt * 16 + li)) * (uint32_t)N +
-            (uint32_t)(tile * 16 + 4 * g)) * 4u;
+    return (((uint32_t)r * (uint32_t)n_tiles + (uint32_t)tile) * (uint32_t)T + (uint32_t)(tt * 16 + li)) * 64u +
+           16u * (uint32_t)g;
   };
   auto in_t = [&](int tt) -> bool { return tt * 16 + li < T; };
 
