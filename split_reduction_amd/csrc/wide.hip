@@ -329,10 +329,14 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
   }
 
   // ---- hand-off of this wave's column ------------------------------------------
+  // Partials: FP32, tile-major [S, N/16, T, 16] (rank r's partial of one
+  // 16-row group is T x 64 contiguous bytes), so a wave's store or read-back
+  // of a token tile covers whole lines.
   const rsrc_t pr = make_rsrc(p.part, (uint32_t)S * (uint32_t)T * (uint32_t)N * 4u);
+  const uint32_t grp0 = (uint32_t)(n0 / 16 + wn * RG);  // this wave's first 16-row group
   auto p_off = [&](int r, int rg, int tt) -> uint32_t {
-    return (((uint32_t)r * (uint32_t)T + (uint32_t)(tt * 16 + li)) * (uint32_t)N +
-            (uint32_t)(n_lane + rg * 16)) * 4u;
+    return (((uint32_t)r * (uint32_t)(N / 16) + grp0 + (uint32_t)rg) * (uint32_t)T + (uint32_t)(tt * 16 + li)) * 64u +
+           16u * (uint32_t)g;
   };
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
