@@ -302,10 +302,13 @@ __global__ __launch_bounds__(64 * WK * WN) void splitk_gemm_kernel(GemmParams p)
   // device-scope atomic. The last arriver reads the other ranks' partials
   // with device-scope coherent loads. No cache-wide writeback or invalidate
   // is needed.
+  // Partials tile-major [S, N/16, T, 16]: a wave's store or load of one
+  // token tile of a 16-row group is 1 KiB of whole lines.
   const rsrc_t pr = make_rsrc(p.part, (uint32_t)S * (uint32_t)T * (uint32_t)N * 4u);
+  const uint32_t grp0 = (uint32_t)((n_lane - 4 * g) / 16);  // this wave's first 16-row group
   auto p_off = [&](int r, int rg, int tt) -> uint32_t {
-    return (((uint32_t)r * (uint32_t)T + (uint32_t)(tt * 16 + li)) * (uint32_t)N +
-            (uint32_t)(n_lane + rg * 16)) * 4u;
+    return (((uint32_t)r * (uint32_t)(N / 16) + grp0 + (uint32_t)rg) * (uint32_t)T + (uint32_t)(tt * 16 + li)) * 64u +
+           16u * (uint32_t)g;
   };
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
