@@ -474,7 +474,7 @@ void splitk_stream_kernel(GemmParams p) {
   // 16-row tile is T x 64 contiguous bytes, so a wave's store or read-back
   // of a token tile covers whole lines (with [S, T, N] it is 16 runs of 64
   // bytes, N * 4 bytes apart). In the mailbox hand-off each value is an
-  // 8-byte (value, tag) pair, token-major [S, T, N].
+  // 8-byte (value, tag) pair in the same order.
   const rsrc_t pr = make_rsrc(p.part, (uint32_t)S * (uint32_t)T * (uint32_t)N * (p.mailbox ? 8u : 4u));
   // Arrival counter of a 16-row tile: one 128-byte line each, so the S
   // ranks' arrivals and the owner's polls of one tile meet no other tile's
@@ -630,14 +630,15 @@ void splitk_stream_kernel(GemmParams p) {
   };
   auto in_t = [&](int tt) -> bool { return tt * 16 + li < T; };
 
-  // Mailbox slot of this lane's quad: element (r, token, feature) is the
-  // 8-byte pair at ((r * T + token) * N + feature) * 8, the quad's four pairs
-  // in two 16-byte halves (page vllm.models.muse_spark.amd.mono.kernels.dev,
+  // Mailbox slot of this lane's quad: element (r, tile, token, f) is the
+  // 8-byte pair at (((r * N/16 + tile) * T + token) * 16 + f) * 8, the same
+  // tile-major order as the plain partials, the quad's four pairs in two
+  // 16-byte halves (page vllm.models.muse_spark.amd.mono.kernels.dev,
   // mb_put2: two (value, tag) pairs per 16-byte store; mb_poll: reload until
   // every tag matches).
   auto m_off = [&](int r, int tile, int tt) -> uint32_t {
-    return (((uint32_t)r * (uint32_t)T + (uint32_t)(tt * 16 + li)) * (uint32_t)N +
-            (uint32_t)(tile * 16 + 4 * g)) * 8u;
+    return (((uint32_t)r * (uint32_t)n_tiles + (uint32_t)tile) * (uint32_t)T + (uint32_t)(tt * 16 + li)) * 128u +
+           32u * (uint32_t)g;
   };
   // This rank's partial of (tile, token tile tt), device-coherent: a plain
   // FP32 quad, or in the mailbox two tagged halves.
