@@ -482,7 +482,19 @@ void splitk_stream_kernel(GemmParams p) {
   auto cnt_of = [&](int tile) { return p.cnt + (size_t)tile * kCntStride; };
 
   // X slot of (load step j, sub-step s, lane K block gg, token t): compact tile.
-  auto x_slot = [&](int j, int s, int gg, int t) -> int { return ((j * SUBS + s) * 4 + gg) * T + t; };
+  // Slot of token t's 8 elements at (step j, sub-step s, lane block gg).
+  // The staging writes give consecutive lanes consecutive K chunks of one
+  // token, T slots apart: with T a power of two that puts 16 lanes on the
+  // same banks. The token index is therefore XOR-ed with the low bits of the
+  // chunk (a permutation of the tokens inside each chunk, at most 16 wide, so
+  // the reads of 16 consecutive tokens stay one 256-byte block). Measured
+  // with conflict-free writes: T=16 staging 3.3 -> 2.1 us, the launch 1 us
+  // shorter (K=N=16384).
+  const int xsw = (T & (T - 1)) == 0 ? (T < 16 ? T : 16) - 1 : 0;
+  auto x_slot = [&](int j, int s, int gg, int t) -> int {
+    const int base = (j * SUBS + s) * 4 + gg;
+    return base * T + (t ^ (base & xsw));
+  };
   f32x4* red_base = reinterpret_cast<f32x4*>(smem + (size_t)T * p.ks * 2);  // 16-byte aligned
   // With p.pdefer, tile k's FP32 partial waits in LDS (after the reduction
   // buffers) until the stream ends: NT * 64 quads per tile.
