@@ -1374,6 +1374,17 @@ constexpr StreamShape kStreamShapes[] = {
     {8, 1, 8, 2, kStreamStorer},    // 6: 7 streaming waves + a storer wave
 };
 constexpr int kNumStreamShapes = sizeof(kStreamShapes) / sizeof(kStreamShapes[0]);
+
+// Load steps in flight per streaming wave. The storer shape on bf16 weights
+// (one line pair per step) keeps fewer than the table's 8: with seven waves
+// streaming one tile's rows, a shallower ring reads the same bytes faster
+// (bit-identical; one box, two runs each, cold single launches: K=N=16384
+// T=1/8/16 86.4-87.7 -> 85.8-86.8 us with 3 steps, T=32 92.2-92.3 ->
+// 90.7 us and T=32 K=7168 N=18432 55.0-55.2 -> 54.3-54.9 us with 4; 2 steps
+// lose 3-4 us at two token tiles, 10 steps lose about 1 us everywhere).
+constexpr int stream_depth(const StreamShape& sh, int nt, int wf) {
+  return (sh.mode == kStreamStorer && wf == kBf16 && sh.c == 2) ? (nt == 1 ? 3 : 4) : sh.d;
+}
 constexpr int kStreamMaxNT = 2;
 constexpr int kStreamMaxX = 128 * 1024;
 constexpr int kClusterMaxGrid = 512;
@@ -1382,7 +1393,7 @@ constexpr long kClusterMaxBatchGrid = 8192;
 template <int NT, int SH, int WF>
 hipError_t launch_stream_one(const Tactic& t, const GemmParams& p, hipStream_t s) {
   constexpr StreamShape sh = kStreamShapes[SH];
-  auto kern = splitk_stream_kernel<NT, sh.wk, sh.wn, sh.d, sh.c, sh.mode, WF>;
+  auto kern = splitk_stream_kernel<NT, sh.wk, sh.wn, stream_depth(sh, NT, WF), sh.c, sh.mode, WF>;
   hipLaunchKernelGGL(kern, dim3(t.grid, p.L), dim3(t.threads), t.lds, s, p);
   return hipGetLastError();
 }
@@ -1455,7 +1466,7 @@ bool stream_fits(int si, int T, int N, int ks, int S, int wf, Tactic* t, int L =
   t->rg = 1;
   t->wk = c.wk;
   t->wn = c.wn;
-  t->d = c.d;
+  t->d = stream_depth(c, t->nt, wf);
   t->c = c.c;
   t->tile_n = 16;
   t->threads = 64 * waves;
