@@ -69,9 +69,13 @@ __global__ __launch_bounds__(64 * kWideWaves) void splitk_wide_kernel(GemmParams
   // at use.
   constexpr int CS2 = CS / 2;                 // ring slots per chunk
   static_assert(CS % 2 == 0, "a chunk holds whole step pairs");
-  // Ring depth in slots (divides CS2): 4 slots = 16 KiB of weights in flight
-  // per wave (bf16), fewer where the decode and its registers are heavier.
-  constexpr int D = MX ? (CS2 < 2 ? CS2 : 2) : 4;
+  // Ring depth in slots (divides CS2): 2 slots = 8 KiB of weights in flight
+  // per wave. With 256 rows streaming per workgroup, more requests in flight
+  // do not read the same bytes any faster (bf16, bit-identical, cold single
+  // launches, one box, three runs each against 4 slots: K=N=16384 T=64
+  // 117.8 against 118.0 us, T=128 126.4 against 127.6 us; 1 slot is slower,
+  // 125-133 us).
+  constexpr int D = CS2 < 2 ? CS2 : 2;
   static_assert(CS2 % D == 0, "ring slots repeat every chunk");
 
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -477,7 +481,7 @@ bool wide_fits(int T, int N, int ks, int S, int wf, Tactic* t) {
   t->rg = 2;
   t->wk = 1;
   t->wn = kWideWaves;
-  t->d = mx ? (nt <= 4 ? 4 : 2) : 8;
+  t->d = mx ? (nt <= 4 ? 4 : 2) : 4;  // load steps in flight per wave (two per ring slot)
   t->c = 1;
   t->kc = kc;
   t->tile_n = kWideRows;
