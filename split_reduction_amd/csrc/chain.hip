@@ -39,10 +39,11 @@ namespace skg {
 namespace {
 
 constexpr int kChainWaves = 8;
-// Load steps in flight per wave (8 KiB of weights at a fold of 2). Measured
-// on the T=8 K=7168 / K=2048 decode chain: 16 steps in flight run slower
-// (eight-step chain 121 against 112.6 us per launch).
-constexpr int kChainDepth = 8;
+// Load steps in flight per wave (4 KiB of weights at a fold of 2). Measured
+// on the T=8 K=7168 / K=2048 decode chain, per step of a 32-step chain, one
+// box: 2 steps 14.7 us, 3 steps 13.1 us, 4 steps 12.8 us, 8 steps 13.9 us;
+// 16 steps were slower still.
+constexpr int kChainDepth = 4;
 
 // s_waitcnt vmcnt(n) for n < 64 (expcnt and lgkmcnt left at their maxima;
 // the count's low four bits sit in bits 3:0 of the immediate, its high two

@@ -58,9 +58,10 @@ struct ConstInt {
 // Block-scaled weights at one token tile keep 3 (each step also carries four
 // activation loads): MXFP4 / MXFP8 T=16 K=7168 N=4096 10.8 -> 10.55 us and
 // 13.8 -> 13.3 us against 4, bit-identical; bf16 with one piece keeps 8
-// (4 or 6 measured slower at T=8 K=7168 N=2048).
+// (4 or 6 measured slower at T=8 K=7168 N=2048), with two pieces 2 (T=1
+// K=1024 N=1024 3.37-3.41 -> 3.31 us against 4).
 constexpr int cluster_depth(int nt, int c, bool mx) {  // mx: block-scaled weights
-  return mx ? (nt == 1 ? 3 : 2) : (nt == 1 ? (c == 2 ? 4 : 8) : (c == 2 ? 2 : 4));
+  return mx ? (nt == 1 ? 3 : 2) : (nt == 1 ? (c == 2 ? 2 : 8) : (c == 2 ? 2 : 4));
 }
 
 }  // namespace
