@@ -440,8 +440,15 @@ bool cluster_fits(int T, int N, int ks, int S, int wf, int max_fold, int force_c
       // no more per rank group than the slice has steps. Eight waves with
       // twice the steps each beat sixteen (measured T=16 K=7168 N=4096:
       // MXFP4 11.7 -> 10.8 us, MXFP8 14.6 -> 14.1 us; bf16 T=8: 8.45 ->
-      // 8.37 us at N=2048, 13.7 -> 13.5 us at N=4096).
-      const int want = S * cs < kClusterMaxWaves ? S * cs : kClusterMaxWaves;
+      // 8.37 us at N=2048, 13.7 -> 13.5 us at N=4096). A single bf16 problem
+      // runs faster still on four (one box, three runs each: T=8 K=7168
+      // N=2048 8.49 -> 8.36 us, T=2 K=4096 N=4096 8.84 -> 8.06 us, T=4..16
+      // K=7168 N=2048..4096 1-2 % faster); block-scaled weights do not
+      // (MXFP8 13.25 -> 13.76 us) and neither do batches (T=8 K=7168 N=2048,
+      // L=8: 5.79 -> 6.02 us a problem), so they keep eight. The cap never
+      // goes below S (each rank group needs a wave).
+      const int cap = (wf != kBf16 || L > 1 || S > 4) ? kClusterMaxWaves : 4;
+      const int want = S * cs < cap ? S * cs : cap;
       int wt = 4;
       while (wt < want) wt *= 2;
       if (wt < S) continue;

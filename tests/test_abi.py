@@ -198,13 +198,14 @@ def test_tactics_cover_the_workloads(T, N, K, S, mx):
 # while the grid still covers the 256 CUs; an unfolded cluster grid below 256
 # workgroups gives way to the persistent kernel; a single problem runs the
 # persistent kernel at one workgroup per CU; cluster workgroups have at most
-# eight waves. Persistent organisation: 7 streaming waves and a storer wave
+# four waves for a single bf16 problem and eight for block-scaled weights and
+# batches. Persistent organisation: 7 streaming waves and a storer wave
 # (shape 6) for single problems with many tiles per workgroup, the partials
 # held in LDS until the stream ends wherever they fit (pdefer) and in the
 # storer's registers where they do not (K=N=16384 T=24/32); the
 # epilogue-wave shape (2) for few tiles per workgroup.
 @pytest.mark.parametrize("T,N,K,S,wf,want", [
-    (8, 2048, 7168, 4, 0, {"kind": "cluster", "fold": 2, "c": 1, "wk": 8, "grid": 256}),
+    (8, 2048, 7168, 4, 0, {"kind": "cluster", "fold": 2, "c": 1, "wk": 4, "grid": 256}),
     (8, 1024, 2048, 2, 0, {"kind": "cluster", "fold": 2, "c": 2}),
     (8, 4096, 7168, 4, 0, {"kind": "cluster", "fold": 1, "c": 2, "grid": 256}),
     (5, 1024, 7168, 4, 0, {"kind": "cluster", "fold": 2, "grid": 128}),
