@@ -57,13 +57,15 @@ struct ConstInt {
 // Load steps kept in flight per wave (operand registers: D * (C + NT*SUBS) * 4).
 // Block-scaled weights at one token tile keep 3 (each step also carries four
 // activation loads): MXFP4 / MXFP8 T=16 K=7168 N=4096 10.8 -> 10.55 us and
-// 13.8 -> 13.3 us against 4, bit-identical; bf16 with one piece keeps 8
-// (4 or 6 measured slower at T=8 K=7168 N=2048); bf16 with two pieces keeps
-// 2 in folds of 4 and 8 (T=1 K=1024 N=1024 3.37-3.41 -> 3.31 us against 4)
-// and 4 below (batches of T=1 K=1024 N=1024: 0.80 against 0.82 us a problem
-// with 2).
-constexpr int cluster_depth(int nt, int c, bool mx, int f) {  // mx: block-scaled weights
-  return mx ? (nt == 1 ? 3 : 2) : (nt == 1 ? (c == 2 ? (f >= 4 ? 2 : 4) : 8) : (c == 2 ? 2 : 4));
+// 13.8 -> 13.3 us against 4, bit-identical; bf16 with one piece keeps 8 in
+// eight-wave workgroups (4 or 6 measured slower at T=8 K=7168 N=2048) and 6
+// in four-wave ones (8.35 -> 8.28 us there; 12 is slower); bf16 with two
+// pieces keeps 2 in folds of 4 and 8 (T=1 K=1024 N=1024 3.37-3.41 -> 3.31 us
+// against 4) and 4 below (batches of T=1 K=1024 N=1024: 0.80 against 0.82 us
+// a problem with 2).
+constexpr int cluster_depth(int nt, int c, bool mx, int f, int wt) {  // mx: block-scaled weights
+  return mx ? (nt == 1 ? 3 : 2)
+            : (nt == 1 ? (c == 2 ? (f >= 4 ? 2 : 4) : (wt <= 4 ? 6 : 8)) : (c == 2 ? 2 : 4));
 }
 
 }  // namespace
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(64 * WT) void splitk_cluster_kernel(GemmParams p) {
   constexpr int PIECE_K = MX ? 4 * LK : 32 * C;  // K elements of one fold of a step
   constexpr int STEP_K = F * PIECE_K;          // K elements of one load step
   constexpr int SUB_K = MX ? 8 : 32 * F;       // K distance between a lane's sub-steps
-  constexpr int D = cluster_depth(NT, C, MX, F);
+  constexpr int D = cluster_depth(NT, C, MX, F, WT);
   // Weight loads in whole 128-byte lines: a fold of F >= 2 already covers
   // 64*F contiguous bytes of each of its R rows per instruction; unfolded
   // bf16 with two pieces loads rows 0-7 and 8-15 as a line pair instead and
@@ -459,7 +461,7 @@ bool cluster_fits(int T, int N, int ks, int S, int wf, int max_fold, int force_c
       t->rg = 1;
       t->wk = wt;
       t->wn = 1;
-      t->d = cluster_depth(nt, c, mx, f);
+      t->d = cluster_depth(nt, c, mx, f, wt);
       t->c = c;
       t->kc = ks;
       t->tile_n = 16 / f;
