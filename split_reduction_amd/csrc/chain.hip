@@ -25,8 +25,10 @@
 //
 // Visibility across the XCDs' caches: C stores are device-coherent (written
 // through to the level all XCDs share) and complete before a workgroup
-// arrives at the barrier; after the barrier an agent-scope acquire fence
-// drops stale copies before the activation loads.
+// arrives at the barrier; the activation loads after the barrier are
+// device-coherent as well, so they never hit a stale copy and need no cache
+// invalidate (measured: a 32-step decode chain 12.7 -> 11.3 us a step against
+// an agent-scope acquire fence after every barrier).
 
 #include "device/mfma.h"
 #include "device/out.h"
@@ -143,7 +145,7 @@ __global__ __launch_bounds__(64 * kChainWaves) void splitk_chain_kernel(ChainPar
     const int xt = lane / (4 * u.F);
     const bool ok = i < u.n_i && xt < T;
     const uint32_t b_row = (uint32_t)(xt < T ? xt : 0) * (uint32_t)u.K * 2u;
-    xb[slot] = ld16_if(ok, u.xr, b_row + (uint32_t)(k_of(u, i) + (lane % (4 * u.F)) * 8) * 2u);
+    xb[slot] = ld16_if<kPolicyDeviceCoherent>(ok, u.xr, b_row + (uint32_t)(k_of(u, i) + (lane % (4 * u.F)) * 8) * 2u);
   };
   auto x_operand = [&](const Unit& u, u32x4 v) -> bf16x8 {
     const int TF = 16 / u.F;
@@ -204,9 +206,9 @@ __global__ __launch_bounds__(64 * kChainWaves) void splitk_chain_kernel(ChainPar
         }
         gen = target;
       }
-      // Stale copies of the previous step's output leave this CU's and this
-      // XCD's caches before any activation load of the next step.
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      // No activation load of the next step moves above the barrier (they
+      // are device-coherent: no stale copy to drop).
+      handoff_order();
     }
     __syncthreads();
   };
