@@ -110,3 +110,34 @@ def test_chain_repeated_launches_and_health():
         for i in range(len(ws)):
             assert np.array_equal(again[i], first[i]), f"rep {rep} step {i}"
     assert sk.skgemm_health()["timeouts"] == 0
+
+
+@pytest.mark.parametrize("T,dims,S", [
+    (8, [7168, 2048, 7168, 2048, 7168, 2048, 7168, 2048, 7168], 4),
+    (5, [1024, 2048, 1024, 3072, 512, 2048], 2),
+    (16, [2048, 1024, 2048, 1024], 8),
+])
+def test_chain_ping_pong_buffers(T, dims, S):
+    """Outputs alternate between two buffers, so step i overwrites the memory
+    that step i-1 read as its activations (every step's C overlaps the C of
+    two steps before). Integer chains: the last two outputs, still held in the
+    two buffers, equal the oracle's chain bit for bit, launch after launch."""
+    t = torch()
+    rng = np.random.default_rng(9990 + T + S)
+    log(f"chain ping-pong T={T} dims={dims} S={S}")
+    x = workloads.to_bf16_bits(rng.integers(-1, 2, size=(T, dims[0])).astype(np.float32))
+    ws = [selection_weights(rng, dims[i + 1], dims[i]) for i in range(len(dims) - 1)]
+    want = G.gemm_chain_ref(x, ws)
+    L = len(ws)
+    width = max(dims[1:])
+    bufs = [t.full((T * width,), SENTINEL, dtype=t.int16, device=DEV) for _ in range(2)]
+    Cs = [bufs[i % 2][:T * dims[i + 1]].view(T, dims[i + 1]).view(t.bfloat16) for i in range(L)]
+    Wd = [to_dev_bf16(w) for w in ws]
+    for rep in range(3):
+        sk.skgemm_bf16_chain(Wd, to_dev_bf16(x), Cs, dims, T, S)
+        t.cuda.synchronize()
+        for i in (L - 2, L - 1):
+            if i < 0:
+                continue
+            got = bf16_bits(Cs[i])
+            assert np.array_equal(F.bf16_bits_to_f64(got), want[i]), f"rep {rep} step {i}"
