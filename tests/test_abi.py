@@ -199,28 +199,31 @@ def test_tactics_cover_the_workloads(T, N, K, S, mx):
 # workgroups gives way to the persistent kernel; a single problem runs the
 # persistent kernel at one workgroup per CU; cluster workgroups have at most
 # four waves for a single bf16 problem and eight for block-scaled weights and
-# batches. Persistent organisation: 7 streaming waves and a storer wave
+# batches. Load steps in flight per wave (d): 6 for one-piece bf16 cluster
+# tiles in four-wave workgroups, 2 for two-piece tiles at folds of 4 and 8, 3
+# for block-scaled tiles, 3 / 4 for the persistent storer shape at one / two
+# token tiles, 4 (two ring slots) in the wide kernel. Persistent organisation: 7 streaming waves and a storer wave
 # (shape 6) for single problems with many tiles per workgroup, the partials
 # held in LDS until the stream ends wherever they fit (pdefer) and in the
 # storer's registers where they do not (K=N=16384 T=24/32); the
 # epilogue-wave shape (2) for few tiles per workgroup.
 @pytest.mark.parametrize("T,N,K,S,wf,want", [
-    (8, 2048, 7168, 4, 0, {"kind": "cluster", "fold": 2, "c": 1, "wk": 4, "grid": 256}),
+    (8, 2048, 7168, 4, 0, {"kind": "cluster", "fold": 2, "c": 1, "wk": 4, "d": 6, "grid": 256}),
     (8, 1024, 2048, 2, 0, {"kind": "cluster", "fold": 2, "c": 2}),
     (8, 4096, 7168, 4, 0, {"kind": "cluster", "fold": 1, "c": 2, "grid": 256}),
     (5, 1024, 7168, 4, 0, {"kind": "cluster", "fold": 2, "grid": 128}),
-    (1, 1024, 1024, 4, 0, {"kind": "cluster", "fold": 4, "c": 2, "grid": 256}),
-    (16, 4096, 7168, 4, 1, {"kind": "cluster", "fold": 1, "wk": 8}),
-    (16, 4096, 7168, 4, 2, {"kind": "cluster", "fold": 1, "wk": 8}),
+    (1, 1024, 1024, 4, 0, {"kind": "cluster", "fold": 4, "c": 2, "d": 2, "grid": 256}),
+    (16, 4096, 7168, 4, 1, {"kind": "cluster", "fold": 1, "wk": 8, "d": 3}),
+    (16, 4096, 7168, 4, 2, {"kind": "cluster", "fold": 1, "wk": 8, "d": 3}),
     (12, 1024, 7168, 4, 0, {"kind": "stream", "grid": 256}),
     (32, 2048, 7168, 4, 0, {"kind": "stream", "grid": 256}),
     (32, 18432, 7168, 8, 0, {"kind": "stream", "grid": 256, "shape": 6, "pdefer": 1}),
-    (8, 16384, 16384, 8, 0, {"kind": "stream", "shape": 6, "pdefer": 1}),
+    (8, 16384, 16384, 8, 0, {"kind": "stream", "shape": 6, "pdefer": 1, "d": 3}),
     (16, 16384, 16384, 8, 0, {"kind": "stream", "shape": 6, "pdefer": 1}),
     (24, 16384, 16384, 8, 0, {"kind": "stream", "shape": 6, "pdefer": 0}),
-    (32, 16384, 16384, 8, 0, {"kind": "stream", "shape": 6, "pdefer": 0}),
+    (32, 16384, 16384, 8, 0, {"kind": "stream", "shape": 6, "pdefer": 0, "d": 4}),
     (12, 1024, 7168, 4, 0, {"kind": "stream", "shape": 2, "pdefer": 0}),
-    (64, 16384, 16384, 4, 0, {"kind": "wide"}),
+    (64, 16384, 16384, 4, 0, {"kind": "wide", "d": 4}),
 ])
 def test_tactic_rules(T, N, K, S, wf, want):
     _ensure_built()
